@@ -1,0 +1,215 @@
+"""Python binding of libmoe_nvfp4.so (the fused NVFP4 MoE layer for MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's gfx950
+kernels.  Functions carry the names of the C entry points declared in
+include/moe_nvfp4.h and take torch tensors (device memory) and the current
+torch stream.  There is no fallback: if the shared library is missing, every
+call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
+
+W4A16 = 0
+W4A4 = 1
+PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+
+OK = 0
+ERR_INVALID_ARG = 1
+ERR_UNSUPPORTED_SHAPE = 2
+ERR_WORKSPACE_TOO_SMALL = 3
+ERR_ARCH = 4
+ERR_HIP = 5
+
+
+class MoeNvfp4Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"moe_nvfp4 status {status}: {msg}")
+        self.status = status
+
+
+class moe_nvfp4_problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "d_model", "d_ff", "num_experts", "top_k", "local_expert_offset",
+        "num_local_experts", "has_shared", "mode", "path")]
+
+
+class moe_nvfp4_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w13", "w13_scale", "w13_global", "w2", "w2_scale", "w2_global")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m nvfp4_expert_layer_amd.build` (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.moe_nvfp4_workspace_size.argtypes = [P(moe_nvfp4_problem), P(sz)]
+        L.moe_nvfp4_validate.argtypes = [P(moe_nvfp4_problem), sz, ctypes.c_char_p]
+        L.moe_nvfp4_forward.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
+                                        P(moe_nvfp4_weights), vp, sz, vp, vp]
+        L.moe_nvfp4_forward_timed.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
+                                              P(moe_nvfp4_weights), vp, sz, vp, vp,
+                                              P(ctypes.c_void_p), ctypes.c_int]
+        L.moe_nvfp4_route.argtypes = [P(moe_nvfp4_problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_nvfp4_quantize_weights.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        L.moe_nvfp4_quantize_activations.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_nvfp4_strerror.argtypes = [ctypes.c_int]
+        L.moe_nvfp4_strerror.restype = ctypes.c_char_p
+        L.moe_nvfp4_last_error.argtypes = []
+        L.moe_nvfp4_last_error.restype = ctypes.c_char_p
+        for f in ("workspace_size", "validate", "forward", "forward_timed", "route", "quantize_weights",
+                  "quantize_activations"):
+            getattr(L, "moe_nvfp4_" + f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != OK:
+        raise MoeNvfp4Error(status, lib().moe_nvfp4_last_error().decode() or
+                            lib().moe_nvfp4_strerror(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_problem(T, d, F, E, k, offset, L, has_shared, mode, path=PATH_AUTO):
+    return moe_nvfp4_problem(T, d, F, E, k, offset, L, int(bool(has_shared)), mode, path)
+
+
+@dataclass
+class NVFP4Experts:
+    """NVFP4 weights of n experts (device tensors), the layout of moe_nvfp4_weights."""
+    w13: torch.Tensor         # uint8 [n, 2F, d/2]
+    w13_scale: torch.Tensor   # uint8 [n, 2F, d/16]
+    w13_global: torch.Tensor  # fp32 [n]
+    w2: torch.Tensor          # uint8 [n, d, F/2]
+    w2_scale: torch.Tensor    # uint8 [n, d, F/16]
+    w2_global: torch.Tensor   # fp32 [n]
+
+    def c_struct(self):
+        return moe_nvfp4_weights(*(t.data_ptr() for t in (
+            self.w13, self.w13_scale, self.w13_global, self.w2, self.w2_scale, self.w2_global)))
+
+    def slice(self, start, count):
+        """Experts [start, start+count) (views; any start is accepted by the library)."""
+        return NVFP4Experts(*(t[start:start + count] for t in (
+            self.w13, self.w13_scale, self.w13_global, self.w2, self.w2_scale, self.w2_global)))
+
+    @staticmethod
+    def empty(n, d, F, device="cuda"):
+        u8 = dict(dtype=torch.uint8, device=device)
+        return NVFP4Experts(torch.empty(n, 2 * F, d // 2, **u8), torch.empty(n, 2 * F, d // 16, **u8),
+                            torch.empty(n, dtype=torch.float32, device=device),
+                            torch.empty(n, d, F // 2, **u8), torch.empty(n, d, F // 16, **u8),
+                            torch.empty(n, dtype=torch.float32, device=device))
+
+
+def moe_nvfp4_strerror(status):
+    return lib().moe_nvfp4_strerror(status).decode()
+
+
+def moe_nvfp4_last_error():
+    return lib().moe_nvfp4_last_error().decode()
+
+
+def moe_nvfp4_workspace_size(problem):
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_nvfp4_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
+    return n.value
+
+
+def moe_nvfp4_validate(problem, workspace_bytes, arch=None):
+    """Returns the status code (does not raise)."""
+    a = arch.encode() if isinstance(arch, str) else arch
+    return lib().moe_nvfp4_validate(ctypes.byref(problem), workspace_bytes, a)
+
+
+def alloc_workspace(problem, device="cuda"):
+    n = moe_nvfp4_workspace_size(problem)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def moe_nvfp4_forward(problem, hidden, gate_w, local, shared, workspace, out, stream=None):
+    """hidden bf16 [T, d]; gate_w bf16 [E, d]; local/shared: NVFP4Experts (shared may be
+    None); workspace uint8 device tensor; out bf16 [T, d] (overwritten)."""
+    lw = local.c_struct()
+    sw = shared.c_struct() if shared is not None else None
+    _check(lib().moe_nvfp4_forward(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), ctypes.byref(lw),
+                                   ctypes.byref(sw) if sw is not None else None, _ptr(workspace),
+                                   workspace.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_nvfp4_forward_timed(problem, hidden, gate_w, local, shared, workspace, out, events,
+                            stream=None):
+    """moe_nvfp4_forward recording raw hipEvent_t handles (ints, or None) at the
+    kernel boundaries; see the header for the event slots."""
+    lw = local.c_struct()
+    sw = shared.c_struct() if shared is not None else None
+    arr = (ctypes.c_void_p * len(events))(*[e if e else None for e in events])
+    _check(lib().moe_nvfp4_forward_timed(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), ctypes.byref(lw),
+                                         ctypes.byref(sw) if sw is not None else None, _ptr(workspace),
+                                         workspace.numel(), _ptr(out), _stream(stream), arr, len(events)))
+    return out
+
+
+def moe_nvfp4_route(problem, hidden, gate_w, workspace, topk_ids=None, topk_w=None, counts=None,
+                    offsets=None, perm=None, stream=None):
+    _check(lib().moe_nvfp4_route(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), _ptr(topk_ids),
+                                 _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+
+
+def moe_nvfp4_quantize_weights(w, codes, scales, global_scale, stream=None):
+    """w bf16 [n, R, C] -> codes uint8 [n, R, C/2], scales uint8 [n, R, C/16], global fp32 [n]."""
+    n, R, C = w.shape
+    _check(lib().moe_nvfp4_quantize_weights(_ptr(w), n, R, C, _ptr(codes), _ptr(scales),
+                                            _ptr(global_scale), _stream(stream)))
+
+
+def moe_nvfp4_quantize_activations(x, codes, scales, stream=None):
+    """x bf16 [R, C] -> codes uint8 [R, C/2], scales uint8 [R, C/16]."""
+    R, C = x.shape
+    _check(lib().moe_nvfp4_quantize_activations(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def quantize_experts(w13, w2, out=None, start=0):
+    """Quantize bf16 expert weights w13 [n, 2F, d], w2 [n, d, F] into `out`
+    (an NVFP4Experts, experts [start, start+n)) on the GPU."""
+    n, twoF, d = w13.shape
+    F = twoF // 2
+    if out is None:
+        out = NVFP4Experts.empty(n, d, F, device=w13.device)
+        start = 0
+    moe_nvfp4_quantize_weights(w13, out.w13[start:start + n], out.w13_scale[start:start + n],
+                               out.w13_global[start:start + n])
+    moe_nvfp4_quantize_weights(w2, out.w2[start:start + n], out.w2_scale[start:start + n],
+                               out.w2_global[start:start + n])
+    return out

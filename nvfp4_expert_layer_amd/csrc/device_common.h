@@ -1,0 +1,146 @@
+// Device-side helpers shared by the gfx950 kernels of the NVFP4 MoE layer.
+//
+// NVFP4 (NVIDIA's format; the page "Serving Solar Open 2 on DGX Spark",
+// section "b12x 버전이 실제 NVFP4 체크포인트를 읽어들이도록 만들기", names its
+// parts: packed FP4 codes, FP8 block scales clamped to 448, per-expert fp32
+// global scale): E2M1 codes two per byte (even element in the low nibble), one
+// E4M3fn scale per 16 elements along K, a fp32 global multiplier per tensor.
+//
+// gfx950 conversion instructions used here (their behaviour was checked on the
+// device for every input byte):
+//   v_cvt_scalef32_pk_bf16_fp4 / _pk_f32_fp4: two E2M1 codes of one byte -> two
+//     bf16 / fp32 values, multiplied by 2^exponent(scale) (only the exponent of
+//     the fp32 scale operand is used).  With scale 1.0 the result is the exact
+//     code value.  byte_sel picks the byte of the source dword.
+//   v_cvt_f32_fp8: one E4M3fn byte -> fp32 (OCP encoding, bias 7, max 448).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace moe {
+
+constexpr int kBlock = 16;          // NVFP4 elements per block scale
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Upper halves of two fp32 values packed as bf16x2 (exact when both values are
+// representable in bf16, which holds for code * E4M3 scale products).
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Two E2M1 codes (byte `sel` of `src`) -> exact fp32 values.
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4x2_to_f32(uint32_t src) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, 1.0f, SEL);
+}
+
+// Eight E2M1 codes (one dword) times a block scale -> 8 exact bf16 (4 dwords).
+__device__ __forceinline__ u32x4_t dequant8_bf16(uint32_t codes, float scale) {
+    f32x2_t a = fp4x2_to_f32<0>(codes), b = fp4x2_to_f32<1>(codes);
+    f32x2_t c = fp4x2_to_f32<2>(codes), d = fp4x2_to_f32<3>(codes);
+    u32x4_t r;
+    r.x = pack_hi16(a[0] * scale, a[1] * scale);
+    r.y = pack_hi16(b[0] * scale, b[1] * scale);
+    r.z = pack_hi16(c[0] * scale, c[1] * scale);
+    r.w = pack_hi16(d[0] * scale, d[1] * scale);
+    return r;
+}
+
+// Eight E2M1 codes -> 8 exact bf16 code values (no scale), 4 dwords.
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16(uint32_t codes) {
+    bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0);
+    bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1);
+    bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2);
+    bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3);
+    u32x4_t r;
+    r.x = __builtin_bit_cast(uint32_t, a);
+    r.y = __builtin_bit_cast(uint32_t, b);
+    r.z = __builtin_bit_cast(uint32_t, c);
+    r.w = __builtin_bit_cast(uint32_t, d);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 encoders (fp32 decisions, round to nearest with ties to the even code,
+// saturating).  Written from the bit layout, not from a table of the host side.
+// ---------------------------------------------------------------------------
+
+// Non-negative finite fp32 -> E4M3fn byte (0x00..0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
+    if (!(v < 448.0f)) return 0x7Eu;                  // saturate (v >= 448)
+    // Smallest normal is 2^-6; below it the grid step is 2^-9 (subnormals).
+    if (v < 0.015625f) {
+        // value = m * 2^-9, m in 0..8 (8 == the first normal 2^-6, code 0x08)
+        float q = v * 512.0f;                           // exact (power-of-two scale)
+        float r = __builtin_rintf(q);                   // ties to even integer = even code
+        return (uint32_t)r;                             // m = 8 encodes as 0x08 (normal 2^-6)
+    }
+    // normal: v = 2^e * (1 + m/8), e in [-6, 8]
+    uint32_t u = __float_as_uint(v);
+    int e = (int)((u >> 23) & 0xFF) - 127;
+    uint32_t mant = u & 0x7FFFFFu;                       // 23-bit fraction
+    // keep 3 fraction bits, round to nearest even on the remaining 20 bits
+    uint32_t keep = mant >> 20;
+    uint32_t rest = mant & 0xFFFFFu;
+    uint32_t code = (uint32_t)((e + 7) << 3) | keep;     // monotone in value
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) code += 1;   // may carry into exponent
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// fp32 -> E2M1 code (4 bits), zero magnitude -> +0.
+__device__ __forceinline__ uint32_t e2m1_encode(float r) {
+    float a = fabsf(r);
+    uint32_t m;
+    // midpoints between {0, .5, 1, 1.5, 2, 3, 4, 6}: .25 .75 1.25 1.75 2.5 3.5 5;
+    // at a midpoint choose the even code.
+    if (a < 0.25f) m = 0;
+    else if (a == 0.25f) m = 0;
+    else if (a < 0.75f) m = 1;
+    else if (a == 0.75f) m = 2;
+    else if (a < 1.25f) m = 2;
+    else if (a == 1.25f) m = 2;
+    else if (a < 1.75f) m = 3;
+    else if (a == 1.75f) m = 4;
+    else if (a < 2.5f) m = 4;
+    else if (a == 2.5f) m = 4;
+    else if (a < 3.5f) m = 5;
+    else if (a == 3.5f) m = 6;
+    else if (a < 5.0f) m = 6;
+    else if (a == 5.0f) m = 6;
+    else m = 7;
+    return (m != 0 && r < 0.0f) ? (m | 8u) : m;
+}
+
+// Wave-wide reductions (wave64).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,376 @@
+// Host engine of the NVFP4 MoE layer: device-free validation, workspace
+// planning, kernel-path dispatch and the C ABI declared in include/moe_nvfp4.h.
+//
+// The boundary follows the page "Serving Solar Open 2 on DGX Spark", section
+// "수정 사항 › b12x에서의 Expert Parallelism 구현 추가": the shard is given by
+// `local_expert_offset` and a count of local experts; the output is a per-shard
+// partial sum; scale tensors of a shard may start at any expert; scratch comes
+// from one caller-owned pool (the workspace) that every layer can reuse; the
+// kernel path is chosen from the shard's expected local load, not the global one.
+#include "../../include/moe_nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MOE_NVFP4_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Path actually used for a problem (AUTO resolved by the expected local load).
+int resolve_path(const moe_nvfp4_problem& p) {
+    if (p.path == MOE_NVFP4_PATH_DECODE || p.path == MOE_NVFP4_PATH_PREFILL) return p.path;
+    // expected local pairs per local expert: T * k / E (uniform routing)
+    const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
+    return per_expert <= 16.0 ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
+}
+
+struct Plan {
+    int KS = 1, path = 1, BM = 16, max_tiles = 0, nblk = 0;
+    size_t rows = 0;  // rows of the expanded (pair + shared) activation space
+    size_t part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
+        ntiles, perm, inv, hq, hq_s, act, act_q, act_s, Y, total;
+};
+
+int check_problem(const moe_nvfp4_problem* p) {
+    if (!p) return fail(MOE_NVFP4_ERR_INVALID_ARG, "problem is NULL");
+    if (p->num_tokens < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "num_tokens < 0");
+    if (p->mode != MOE_NVFP4_W4A16 && p->mode != MOE_NVFP4_W4A4)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown mode %d", p->mode);
+    if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_PREFILL)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown path %d", p->path);
+    if (p->has_shared != 0 && p->has_shared != 1)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "has_shared must be 0 or 1");
+    if (p->num_experts < 1 || p->num_experts > 1024)
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "num_experts %d outside 1..1024", p->num_experts);
+    if (p->top_k < 1 || p->top_k > 32 || p->top_k > p->num_experts)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "top_k %d outside 1..min(E, 32)", p->top_k);
+    if (p->num_local_experts < 1) return fail(MOE_NVFP4_ERR_INVALID_ARG, "num_local_experts < 1");
+    if (p->local_expert_offset < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "local_expert_offset < 0");
+    if ((long long)p->local_expert_offset + p->num_local_experts > p->num_experts)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "local_expert_offset + num_local_experts > num_experts");
+    if (p->d_model < 128 || p->d_model > 16384 || p->d_model % 128)
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_model %d: need a multiple of 128 in 128..16384",
+                    p->d_model);
+    if (p->d_ff < 128 || p->d_ff > 16384 || p->d_ff % 128)
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_ff %d: need a multiple of 128 in 128..16384", p->d_ff);
+    // index arithmetic: pair rows and per-row offsets stay within int32
+    const long long rows = (long long)p->num_tokens * (p->top_k + 1);
+    if (rows > (1LL << 27)) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "num_tokens * (top_k + 1) > 2^27");
+    return MOE_NVFP4_OK;
+}
+
+void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
+    const size_t T = p.num_tokens, k = p.top_k, E = p.num_experts, L = p.num_local_experts;
+    const size_t d = p.d_model, F = p.d_ff;
+    pl.KS = moe::router_ksplit((int)T, (int)E, (int)d);
+    pl.path = resolve_path(p);
+    pl.BM = moe::gemm_bm(pl.path);
+    const size_t bm = pl.BM;
+    pl.max_tiles = (int)((T * k + bm - 1) / bm + L + (p.has_shared ? (T + bm - 1) / bm : 0));
+    pl.nblk = (int)((T + 255) / 256);
+    pl.rows = T * k + (p.has_shared ? T : 0);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
+    pl.part = take((size_t)pl.KS * T * E * 4);
+    pl.xn2 = take((size_t)pl.KS * T * 8);
+    pl.gn2 = take((size_t)pl.KS * E * 8);
+    pl.topk_ids = take(T * k * 4);
+    pl.topk_w = take(T * k * 4);
+    pl.local_ids = take(T * k * 4);
+    pl.rank = take(T * k * 4);
+    pl.block_counts = take((size_t)pl.nblk * L * 4);
+    pl.counts = take(L * 4);
+    pl.offsets = take((L + 1) * 4);
+    pl.tiles = take((size_t)pl.max_tiles * 16);
+    pl.ntiles = take(4);
+    pl.perm = take(T * k * 4);
+    pl.inv = take(T * k * 4);
+    const bool w4a4 = p.mode == MOE_NVFP4_W4A4;
+    pl.hq = take(w4a4 ? T * d / 2 : 0);
+    pl.hq_s = take(w4a4 ? T * d / 16 : 0);
+    pl.act = take(w4a4 ? 0 : pl.rows * F * 2);
+    pl.act_q = take(w4a4 ? pl.rows * F / 2 : 0);
+    pl.act_s = take(w4a4 ? pl.rows * F / 16 : 0);
+    pl.Y = take(pl.rows * d * 4);
+    pl.total = o;
+}
+
+bool arch_ok(const char* arch) { return arch && std::strncmp(arch, "gfx950", 6) == 0; }
+
+// Architecture of the current device, cached per device id.
+int current_arch_ok(int* dev_out) {
+    static std::mutex mu;
+    static int cache[64];  // 0 unknown, 1 gfx950, 2 other
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MOE_NVFP4_ERR_HIP, "hipGetDevice failed");
+    *dev_out = dev;
+    if (dev < 0 || dev >= 64) return fail(MOE_NVFP4_ERR_HIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MOE_NVFP4_ERR_HIP, "hipGetDeviceProperties failed");
+        cache[dev] = arch_ok(prop.gcnArchName) ? 1 : 2;
+    }
+    if (cache[dev] != 1) return fail(MOE_NVFP4_ERR_ARCH, "device %d is not gfx950", dev);
+    return MOE_NVFP4_OK;
+}
+
+int check_weights(const moe_nvfp4_weights* w, const char* what) {
+    if (!w) return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s weights are NULL", what);
+    if (!w->w13 || !w->w13_scale || !w->w13_global || !w->w2 || !w->w2_scale || !w->w2_global)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s weights have a NULL tensor pointer", what);
+    return MOE_NVFP4_OK;
+}
+
+moe::ExpertWeights to_internal(const moe_nvfp4_weights* w) {
+    moe::ExpertWeights e{};
+    if (w) {
+        e.w13 = w->w13; e.w13_s = w->w13_scale; e.g13 = w->w13_global;
+        e.w2 = w->w2; e.w2_s = w->w2_scale; e.g2 = w->w2_global;
+    }
+    return e;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int hip_status(hipError_t e, const char* where) {
+    if (e != hipSuccess) return fail(MOE_NVFP4_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+    return MOE_NVFP4_OK;
+}
+
+// Routing + permutation into the workspace (or the caller's buffers where given).
+int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, const void* gate_w,
+              void* ws, hipStream_t s, int32_t* ids_out, float* w_out, int32_t* counts_out,
+              int32_t* offsets_out, int32_t* perm_out) {
+    moe::RouterArgs r{};
+    r.X = static_cast<const uint16_t*>(hidden);
+    r.G = static_cast<const uint16_t*>(gate_w);
+    r.T = p.num_tokens; r.E = p.num_experts; r.d = p.d_model; r.KS = pl.KS; r.topk = p.top_k;
+    r.offset = p.local_expert_offset; r.L = p.num_local_experts;
+    r.part = at<float>(ws, pl.part); r.xn2 = at<double>(ws, pl.xn2); r.gn2 = at<double>(ws, pl.gn2);
+    r.topk_ids = ids_out ? ids_out : at<int32_t>(ws, pl.topk_ids);
+    r.topk_w = w_out ? w_out : at<float>(ws, pl.topk_w);
+    r.local_ids = at<int32_t>(ws, pl.local_ids);
+    int st = hip_status(moe::launch_router(r, s), "router launch");
+    if (st) return st;
+    moe::PermArgs q{};
+    q.local_ids = r.local_ids; q.T = p.num_tokens; q.topk = p.top_k; q.L = p.num_local_experts;
+    q.has_shared = p.has_shared; q.BM = pl.BM; q.max_tiles = pl.max_tiles;
+    q.block_counts = at<int32_t>(ws, pl.block_counts); q.rank = at<int32_t>(ws, pl.rank);
+    q.counts = counts_out ? counts_out : at<int32_t>(ws, pl.counts);
+    q.offsets = offsets_out ? offsets_out : at<int32_t>(ws, pl.offsets);
+    q.tiles = at<int4>(ws, pl.tiles); q.ntiles = at<int32_t>(ws, pl.ntiles);
+    q.perm = perm_out ? perm_out : at<int32_t>(ws, pl.perm); q.inv = at<int32_t>(ws, pl.inv);
+    return hip_status(moe::launch_permute(q, s), "permutation launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_nvfp4_strerror(int status) {
+    switch (status) {
+        case MOE_NVFP4_OK: return "ok";
+        case MOE_NVFP4_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_NVFP4_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case MOE_NVFP4_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_NVFP4_ERR_ARCH: return "device architecture is not gfx950";
+        case MOE_NVFP4_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+int moe_nvfp4_workspace_size(const moe_nvfp4_problem* p, size_t* bytes) {
+    if (!bytes) return fail(MOE_NVFP4_ERR_INVALID_ARG, "bytes is NULL");
+    int st = check_problem(p);
+    if (st) return st;
+    Plan pl;
+    make_plan(*p, pl);
+    *bytes = pl.total;
+    return ok();
+}
+
+int moe_nvfp4_validate(const moe_nvfp4_problem* p, size_t workspace_bytes, const char* arch) {
+    int st = check_problem(p);
+    if (st) return st;
+    Plan pl;
+    make_plan(*p, pl);
+    if (workspace_bytes < pl.total)
+        return fail(MOE_NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes,
+                    pl.total);
+    if (arch && !arch_ok(arch)) return fail(MOE_NVFP4_ERR_ARCH, "architecture '%s' is not gfx950", arch);
+    return ok();
+}
+
+int moe_nvfp4_forward(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w,
+                      const moe_nvfp4_weights* local, const moe_nvfp4_weights* shared, void* workspace,
+                      size_t workspace_bytes, void* out, void* stream) {
+    return moe_nvfp4_forward_timed(p, hidden, gate_w, local, shared, workspace, workspace_bytes, out, stream,
+                                   nullptr, 0);
+}
+
+int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w,
+                            const moe_nvfp4_weights* local, const moe_nvfp4_weights* shared, void* workspace,
+                            size_t workspace_bytes, void* out, void* stream, void* const* events,
+                            int num_events) {
+    if (num_events < 0 || num_events > 6 || (num_events > 0 && !events))
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "num_events must be 0..6 with a non-NULL array");
+    int st = moe_nvfp4_validate(p, workspace_bytes, nullptr);
+    if (st) return st;
+    if (!hidden || !gate_w || !out) return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w/out is NULL");
+    if ((st = check_weights(local, "local"))) return st;
+    if (p->has_shared) {
+        if ((st = check_weights(shared, "shared"))) return st;
+    } else if (shared) {
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "shared weights given but has_shared == 0");
+    }
+    Plan pl;
+    make_plan(*p, pl);
+    if (!workspace && pl.total) return fail(MOE_NVFP4_ERR_INVALID_ARG, "workspace is NULL");
+    int dev;
+    if ((st = current_arch_ok(&dev))) return st;
+    if (p->num_tokens == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> int {
+        if (i < num_events && events[i])
+            return hip_status(hipEventRecord(static_cast<hipEvent_t>(events[i]), s), "hipEventRecord");
+        return MOE_NVFP4_OK;
+    };
+    if ((st = mark(0))) return st;
+    if ((st = run_route(*p, pl, hidden, gate_w, workspace, s, nullptr, nullptr, nullptr, nullptr, nullptr)))
+        return st;
+    if ((st = mark(1))) return st;
+    const bool w4a4 = p->mode == MOE_NVFP4_W4A4;
+    if (w4a4) {
+        st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
+                                                 p->d_model, at<uint8_t>(workspace, pl.hq),
+                                                 at<uint8_t>(workspace, pl.hq_s), s),
+                        "activation quantizer launch");
+        if (st) return st;
+    }
+    if ((st = mark(2))) return st;
+    moe::GemmArgs g{};
+    g.T = p->num_tokens; g.d = p->d_model; g.F = p->d_ff; g.topk = p->top_k; g.L = p->num_local_experts;
+    g.mode = p->mode;
+    g.perm = at<int32_t>(workspace, pl.perm);
+    g.tiles = at<int4>(workspace, pl.tiles);
+    g.ntiles = at<int32_t>(workspace, pl.ntiles);
+    g.max_tiles = pl.max_tiles;
+    g.hidden = static_cast<const uint16_t*>(hidden);
+    g.hq = at<uint8_t>(workspace, pl.hq);
+    g.hq_s = at<uint8_t>(workspace, pl.hq_s);
+    g.local = to_internal(local);
+    g.shared = to_internal(p->has_shared ? shared : nullptr);
+    g.act = at<uint16_t>(workspace, pl.act);
+    g.act_q = at<uint8_t>(workspace, pl.act_q);
+    g.act_s = at<uint8_t>(workspace, pl.act_s);
+    g.Y = at<float>(workspace, pl.Y);
+    if ((st = hip_status(moe::launch_gemm1(g, pl.path, s), "gemm1 launch"))) return st;
+    if ((st = mark(3))) return st;
+    if ((st = hip_status(moe::launch_gemm2(g, pl.path, s), "gemm2 launch"))) return st;
+    if ((st = mark(4))) return st;
+    moe::CombineArgs c{};
+    c.T = p->num_tokens; c.d = p->d_model; c.topk = p->top_k; c.has_shared = p->has_shared;
+    c.topk_w = at<float>(workspace, pl.topk_w);
+    c.inv = at<int32_t>(workspace, pl.inv);
+    c.Y = g.Y;
+    c.out = static_cast<uint16_t*>(out);
+    if ((st = hip_status(moe::launch_combine(c, s), "combine launch"))) return st;
+    if ((st = mark(5))) return st;
+    return ok();
+}
+
+int moe_nvfp4_route(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w, int32_t* topk_ids,
+                    float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = moe_nvfp4_validate(p, workspace_bytes, nullptr);
+    if (st) return st;
+    if (!hidden || !gate_w) return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w is NULL");
+    Plan pl;
+    make_plan(*p, pl);
+    if (!workspace && pl.total) return fail(MOE_NVFP4_ERR_INVALID_ARG, "workspace is NULL");
+    int dev;
+    if ((st = current_arch_ok(&dev))) return st;
+    if (p->num_tokens == 0) {
+        // counts = 0, offsets = 0 still have to be written
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (counts && (st = hip_status(moe::launch_fill_u32(reinterpret_cast<uint32_t*>(counts),
+                                                             (size_t)p->num_local_experts, 0u, s), "fill")))
+            return st;
+        if (offsets && (st = hip_status(moe::launch_fill_u32(reinterpret_cast<uint32_t*>(offsets),
+                                                              (size_t)p->num_local_experts + 1, 0u, s), "fill")))
+            return st;
+        return ok();
+    }
+    st = run_route(*p, pl, hidden, gate_w, workspace, static_cast<hipStream_t>(stream), topk_ids, topk_w,
+                   counts, offsets, perm);
+    if (st) return st;
+    return ok();
+}
+
+int moe_nvfp4_quantize_weights(const void* w, int32_t n, int32_t R, int32_t C, uint8_t* codes,
+                               uint8_t* scales, float* global, void* stream) {
+    if (!w || !codes || !scales || !global) return fail(MOE_NVFP4_ERR_INVALID_ARG, "NULL pointer");
+    if (n < 0 || R < 0 || C < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "negative size");
+    if (C % 16) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "C %d is not a multiple of 16", C);
+    if ((long long)n * R * C > (1LL << 40)) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "tensor too large");
+    int dev, st;
+    if ((st = current_arch_ok(&dev))) return st;
+    if (n == 0 || R == 0 || C == 0) {
+        // all-zero (empty) tensors: global scale 1, as for any all-zero tensor
+        if (n > 0 && (st = hip_status(moe::launch_fill_u32(reinterpret_cast<uint32_t*>(global), (size_t)n,
+                                                            0x3F800000u, static_cast<hipStream_t>(stream)),
+                                       "fill")))
+            return st;
+        return ok();
+    }
+    st = hip_status(moe::launch_quantize_weights(static_cast<const uint16_t*>(w), n, R, C, codes, scales, global,
+                                                 static_cast<hipStream_t>(stream)),
+                    "weight quantizer launch");
+    return st ? st : ok();
+}
+
+int moe_nvfp4_quantize_activations(const void* x, int32_t R, int32_t C, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+    if (!x || !codes || !scales) return fail(MOE_NVFP4_ERR_INVALID_ARG, "NULL pointer");
+    if (R < 0 || C < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "negative size");
+    if (C % 16) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "C %d is not a multiple of 16", C);
+    int dev, st;
+    if ((st = current_arch_ok(&dev))) return st;
+    st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(x), R, C, codes, scales,
+                                             static_cast<hipStream_t>(stream)),
+                    "activation quantizer launch");
+    return st ? st : ok();
+}
+
+}  // extern "C"

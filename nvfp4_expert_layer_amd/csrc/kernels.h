@@ -1,0 +1,79 @@
+// Internal interface between the host engine and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct ExpertWeights {            // device pointers, n experts, expert-major
+    const uint8_t* w13;           // [n][2F][d/2]
+    const uint8_t* w13_s;         // [n][2F][d/16]
+    const float* g13;             // [n]
+    const uint8_t* w2;            // [n][d][F/2]
+    const uint8_t* w2_s;          // [n][d][F/16]
+    const float* g2;              // [n]
+};
+
+struct RouterArgs {
+    const uint16_t* X;            // bf16 [T][d]
+    const uint16_t* G;            // bf16 [E][d]
+    int T, E, d, KS, topk, offset, L;
+    float* part;                  // [KS][T][E]
+    double* xn2;                  // [KS][T]
+    double* gn2;                  // [KS][E]
+    int32_t* topk_ids;            // [T][k]
+    float* topk_w;                // [T][k]
+    int32_t* local_ids;           // [T][k]
+};
+
+struct PermArgs {
+    const int32_t* local_ids;     // [T][k]
+    int T, topk, L, has_shared, BM, max_tiles;
+    int32_t* block_counts;        // [nblk][L]  (becomes per-block bases)
+    int32_t* rank;                // [T][k]
+    int32_t* counts;              // [L]
+    int32_t* offsets;             // [L+1]
+    int4* tiles;                  // [max_tiles]
+    int32_t* ntiles;              // [1]
+    int32_t* perm;                // [T*k]
+    int32_t* inv;                 // [T*k]
+};
+
+struct GemmArgs {
+    int T, d, F, topk, L, mode;
+    const int32_t* perm;          // [T*k]
+    const int4* tiles;            // (group, row_begin, row_end, -)
+    const int32_t* ntiles;
+    int max_tiles;
+    const uint16_t* hidden;       // bf16 [T][d]
+    const uint8_t* hq;            // W4A4 hidden codes  [T][d/2]
+    const uint8_t* hq_s;          // W4A4 hidden scales [T][d/16]
+    ExpertWeights local, shared;
+    uint16_t* act;                // W4A16: bf16 [R][F];  R = T*k + T
+    uint8_t* act_q;               // W4A4:  codes [R][F/2]
+    uint8_t* act_s;               // W4A4:  scales [R][F/16]
+    float* Y;                     // fp32 [R][d]
+};
+
+struct CombineArgs {
+    int T, d, topk, has_shared;
+    const float* topk_w;          // [T][k]
+    const int32_t* inv;           // [T][k] row of each pair, -1 dropped
+    const float* Y;               // [R][d]
+    uint16_t* out;                // bf16 [T][d]
+};
+
+int router_ksplit(int T, int E, int d);
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+hipError_t launch_permute(const PermArgs& a, hipStream_t s);
+hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, uint8_t* scales,
+                               hipStream_t s);
+hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
+                                   uint8_t* scales, float* global, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+int gemm_bm(int path);            // rows per tile of the chosen path
+hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s);
+hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the header
+declares, and its device-free validation reports every error class."""
+import os
+import re
+
+import pytest
+
+import nvfp4_expert_layer_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_nvfp4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nv.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_and_last_error():
+    assert nv.moe_nvfp4_strerror(0) == "ok"
+    assert "workspace" in nv.moe_nvfp4_strerror(nv.ERR_WORKSPACE_TOO_SMALL)
+    assert nv.moe_nvfp4_strerror(99) == "unknown status"
+
+
+def good():
+    return nv.make_problem(64, 4096, 1024, 320, 8, 0, 160, True, nv.W4A16)
+
+
+def test_workspace_size_and_validation_ok():
+    p = good()
+    n = nv.moe_nvfp4_workspace_size(p)
+    assert n > 64 * 8 * 4096 * 4              # at least the per-pair fp32 staging
+    assert nv.moe_nvfp4_validate(p, n, "gfx950:sramecc+:xnack-") == nv.OK
+    assert nv.moe_nvfp4_validate(p, n, None) == nv.OK
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_tokens", -1, nv.ERR_INVALID_ARG),
+    ("mode", 7, nv.ERR_INVALID_ARG),
+    ("path", 9, nv.ERR_INVALID_ARG),
+    ("has_shared", 2, nv.ERR_INVALID_ARG),
+    ("top_k", 0, nv.ERR_INVALID_ARG),
+    ("top_k", 33, nv.ERR_INVALID_ARG),
+    ("num_local_experts", 0, nv.ERR_INVALID_ARG),
+    ("local_expert_offset", -1, nv.ERR_INVALID_ARG),
+    ("local_expert_offset", 161, nv.ERR_INVALID_ARG),          # 161 + 160 > 320
+    ("num_experts", 2000, nv.ERR_UNSUPPORTED_SHAPE),
+    ("d_model", 4000, nv.ERR_UNSUPPORTED_SHAPE),
+    ("d_ff", 1000, nv.ERR_UNSUPPORTED_SHAPE),
+    ("d_model", 64, nv.ERR_UNSUPPORTED_SHAPE),
+])
+def test_validation_errors(field, value, status):
+    p = good()
+    setattr(p, field, value)
+    assert nv.moe_nvfp4_validate(p, 1 << 40, None) == status
+    assert nv.moe_nvfp4_last_error() != ""
+
+
+def test_top_k_above_num_experts_and_any_offset_binds():
+    p = nv.make_problem(4, 256, 128, 6, 7, 0, 6, False, nv.W4A16)
+    assert nv.moe_nvfp4_validate(p, 1 << 40, None) == nv.ERR_INVALID_ARG
+    # any shard offset (scale tensors need no 16-expert alignment)
+    for off in (0, 1, 3, 159, 160, 317):
+        p = nv.make_problem(64, 4096, 1024, 320, 8, off, 320 - off if off > 160 else 3, True, nv.W4A4)
+        assert nv.moe_nvfp4_validate(p, 1 << 40, None) == nv.OK
+
+
+def test_workspace_too_small_and_arch():
+    p = good()
+    n = nv.moe_nvfp4_workspace_size(p)
+    assert nv.moe_nvfp4_validate(p, n - 1, None) == nv.ERR_WORKSPACE_TOO_SMALL
+    assert nv.moe_nvfp4_validate(p, n, "gfx942:sramecc+:xnack-") == nv.ERR_ARCH
+    assert nv.moe_nvfp4_validate(p, n, "sm_121") == nv.ERR_ARCH
+
+
+def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
+    small = nv.moe_nvfp4_workspace_size(nv.make_problem(64, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4))
+    big = nv.moe_nvfp4_workspace_size(nv.make_problem(8192, 4096, 1024, 320, 8, 0, 320, True, nv.W4A4))
+    assert big > small
+    p = nv.make_problem(0, 4096, 1024, 320, 8, 0, 160, True, nv.W4A16)
+    assert nv.moe_nvfp4_validate(p, nv.moe_nvfp4_workspace_size(p), None) == nv.OK
