@@ -75,11 +75,23 @@ def _round_to_grid(v, grid):
 
 def e2m1_encode(r):
     """fp32/fp64 values -> 4-bit codes, round-to-nearest-even, saturating at 6.
-    Zero magnitude (after rounding) gives code 0 (+0)."""
-    r = np.asarray(r, dtype=np.float64)
-    mag_code = _round_to_grid(np.abs(r), _E2M1_MAG)
+    Zero magnitude (after rounding) gives code 0 (+0).
+
+    The magnitude code is the number of midpoints between neighbouring grid
+    values that |r| lies above; at a midpoint exactly, it rounds up only when
+    the upper neighbour has an even code.  Values past the last midpoint get
+    code 7 (6.0), which is the saturation."""
+    r = np.asarray(r)
+    if r.dtype != np.float64:
+        r = r.astype(np.float32)
+    a = np.abs(r)
+    mag_code = np.zeros(a.shape, dtype=np.uint8)
+    for i in range(7):
+        mid = (_E2M1_MAG[i] + _E2M1_MAG[i + 1]) * 0.5      # exact in fp32 and fp64
+        up = (a >= mid) if (i + 1) % 2 == 0 else (a > mid)
+        mag_code += up.astype(np.uint8)
     sign = (r < 0) & (mag_code != 0)
-    return (mag_code | np.where(sign, 8, 0)).astype(np.uint8)
+    return mag_code | np.where(sign, np.uint8(8), np.uint8(0))
 
 
 # ----------------------------------------------------------------------------
