@@ -131,6 +131,18 @@ __device__ __forceinline__ uint32_t e2m1_encode(float r) {
     return (m != 0 && r < 0.0f) ? (m | 8u) : m;
 }
 
+// E2M1 code (4 bits) -> its exact fp32 value.
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code & 0xFu, 1.0f, 0)[0];
+}
+
+// NVFP4 quantize-dequantize of one value given its block's amax (W4A4 rule:
+// scale = E4M3(amax / 6), code = E2M1(x / scale)); returns code * scale exactly.
+__device__ __forceinline__ float nvfp4_fake_quant(float x, float block_amax) {
+    const float s = e4m3_to_f32(e4m3_encode_nonneg(__fdiv_rn(block_amax, 6.0f)));
+    return s > 0.0f ? e2m1_value(e2m1_encode(__fdiv_rn(x, s))) * s : 0.0f;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll

@@ -54,7 +54,7 @@ struct Plan {
     int KS = 1, path = 1, BM = 16, max_tiles = 0, nblk = 0;
     size_t rows = 0;  // rows of the expanded (pair + shared) activation space
     size_t part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
-        ntiles, perm, inv, hq, hq_s, act, act_q, act_s, Y, total;
+        ntiles, perm, inv, hq, act, Y, total;
 };
 
 int check_problem(const moe_nvfp4_problem* p) {
@@ -112,11 +112,8 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.perm = take(T * k * 4);
     pl.inv = take(T * k * 4);
     const bool w4a4 = p.mode == MOE_NVFP4_W4A4;
-    pl.hq = take(w4a4 ? T * d / 2 : 0);
-    pl.hq_s = take(w4a4 ? T * d / 16 : 0);
-    pl.act = take(w4a4 ? 0 : pl.rows * F * 2);
-    pl.act_q = take(w4a4 ? pl.rows * F / 2 : 0);
-    pl.act_s = take(w4a4 ? pl.rows * F / 16 : 0);
+    pl.hq = take(w4a4 ? T * d * 2 : 0);
+    pl.act = take(pl.rows * F * 2);
     pl.Y = take(pl.rows * d * 4);
     pl.total = o;
 }
@@ -272,9 +269,8 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     if ((st = mark(1))) return st;
     const bool w4a4 = p->mode == MOE_NVFP4_W4A4;
     if (w4a4) {
-        st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
-                                                 p->d_model, at<uint8_t>(workspace, pl.hq),
-                                                 at<uint8_t>(workspace, pl.hq_s), s),
+        st = hip_status(moe::launch_fake_quant_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
+                                                   p->d_model, at<uint16_t>(workspace, pl.hq), s),
                         "activation quantizer launch");
         if (st) return st;
     }
@@ -287,17 +283,17 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     g.ntiles = at<int32_t>(workspace, pl.ntiles);
     g.max_tiles = pl.max_tiles;
     g.hidden = static_cast<const uint16_t*>(hidden);
-    g.hq = at<uint8_t>(workspace, pl.hq);
-    g.hq_s = at<uint8_t>(workspace, pl.hq_s);
+    g.hq = at<uint16_t>(workspace, pl.hq);
     g.local = to_internal(local);
     g.shared = to_internal(p->has_shared ? shared : nullptr);
     g.act = at<uint16_t>(workspace, pl.act);
-    g.act_q = at<uint8_t>(workspace, pl.act_q);
-    g.act_s = at<uint8_t>(workspace, pl.act_s);
     g.Y = at<float>(workspace, pl.Y);
-    if ((st = hip_status(moe::launch_gemm1(g, pl.path, s), "gemm1 launch"))) return st;
+    const bool dec = pl.path == MOE_NVFP4_PATH_DECODE;
+    if ((st = hip_status(dec ? moe::launch_dec_gemm1(g, s) : moe::launch_gemm1(g, pl.path, s), "gemm1 launch")))
+        return st;
     if ((st = mark(3))) return st;
-    if ((st = hip_status(moe::launch_gemm2(g, pl.path, s), "gemm2 launch"))) return st;
+    if ((st = hip_status(dec ? moe::launch_dec_gemm2(g, s) : moe::launch_gemm2(g, pl.path, s), "gemm2 launch")))
+        return st;
     if ((st = mark(4))) return st;
     moe::CombineArgs c{};
     c.T = p->num_tokens; c.d = p->d_model; c.topk = p->top_k; c.has_shared = p->has_shared;

@@ -107,9 +107,7 @@ __global__ __launch_bounds__(256) void gemm1_swiglu_kernel(GemmArgs a) {
                 uint16_t* dst = &As[r][kc];
                 int t = atok[i];
                 if (t < 0) zero_chunk(dst);
-                else if (MODE == 0) stage_bf16_chunk(dst, a.hidden + (size_t)t * d + k0 + kc);
-                else stage_fp4_chunk(dst, a.hq + (size_t)t * (d / 2) + (k0 + kc) / 2,
-                                     a.hq_s[(size_t)t * (d / 16) + (k0 + kc) / 16]);
+                else stage_bf16_chunk(dst, (MODE == 0 ? a.hidden : a.hq) + (size_t)t * d + k0 + kc);
             }
         }
 #pragma unroll
@@ -154,27 +152,18 @@ __global__ __launch_bounds__(256) void gemm1_swiglu_kernel(GemmArgs a) {
                 const int row = rb + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + q;
                 const float gt = acc[i][j][q] * g13;
                 const float up = acc[i][CT + j][q] * g13;
-                const float av = silu_f32(gt) * up;
-                const bool valid = row < re;
-                if (MODE == 0) {
-                    if (valid) a.act[(size_t)row * F + col] = (uint16_t)f32_to_bf16_rne(av);
-                } else {
-                    // NVFP4-quantize 16 consecutive columns held by the 16 lanes of this row group
+                float av = silu_f32(gt) * up;
+                if (MODE == 1) {
+                    // NVFP4 quantize-dequantize over the 16 consecutive columns held
+                    // by the 16 lanes of this row group
                     float m = fabsf(av);
                     m = fmaxf(m, __shfl_xor(m, 1, 64));
                     m = fmaxf(m, __shfl_xor(m, 2, 64));
                     m = fmaxf(m, __shfl_xor(m, 4, 64));
                     m = fmaxf(m, __shfl_xor(m, 8, 64));
-                    const uint32_t sb = e4m3_encode_nonneg(__fdiv_rn(m, 6.0f));
-                    const float s = e4m3_to_f32(sb);
-                    const uint32_t c = s > 0.0f ? e2m1_encode(__fdiv_rn(av, s)) : 0u;
-                    const uint32_t other = __shfl_xor(c, 1, 64);
-                    if (valid) {
-                        if ((lane & 1) == 0)
-                            a.act_q[(size_t)row * (F / 2) + col / 2] = (uint8_t)(c | (other << 4));
-                        if ((lane & 15) == 0) a.act_s[(size_t)row * (F / 16) + col / 16] = (uint8_t)sb;
-                    }
+                    av = nvfp4_fake_quant(av, m);
                 }
+                if (row < re) a.act[(size_t)row * F + col] = (uint16_t)f32_to_bf16_rne(av);
             }
         }
     }
@@ -225,9 +214,7 @@ __global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
                 int gr = rb + r;
                 uint16_t* dst = &As[r][kc];
                 if (gr >= re) zero_chunk(dst);
-                else if (MODE == 0) stage_bf16_chunk(dst, a.act + (size_t)gr * F + k0 + kc);
-                else stage_fp4_chunk(dst, a.act_q + (size_t)gr * (F / 2) + (k0 + kc) / 2,
-                                     a.act_s[(size_t)gr * (F / 16) + (k0 + kc) / 16]);
+                else stage_bf16_chunk(dst, a.act + (size_t)gr * F + k0 + kc);
             }
         }
 #pragma unroll
@@ -326,13 +313,8 @@ hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s) {
 
 hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s) {
     dim3 grid(a.max_tiles, a.d / 128);
-    if (path == 1) {
-        if (a.mode == 0) hipLaunchKernelGGL((gemm2_kernel<16, 1, 0>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm2_kernel<16, 1, 1>), grid, dim3(256), 0, s, a);
-    } else {
-        if (a.mode == 0) hipLaunchKernelGGL((gemm2_kernel<64, 4, 0>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm2_kernel<64, 4, 1>), grid, dim3(256), 0, s, a);
-    }
+    if (path == 1) hipLaunchKernelGGL((gemm2_kernel<16, 1, 0>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm2_kernel<64, 4, 0>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -46,13 +46,10 @@ struct GemmArgs {
     const int32_t* ntiles;
     int max_tiles;
     const uint16_t* hidden;       // bf16 [T][d]
-    const uint8_t* hq;            // W4A4 hidden codes  [T][d/2]
-    const uint8_t* hq_s;          // W4A4 hidden scales [T][d/16]
+    const uint16_t* hq;           // W4A4: hidden NVFP4-quantized, exact dequantized bf16 [T][d]
     ExpertWeights local, shared;
-    uint16_t* act;                // W4A16: bf16 [R][F];  R = T*k + T
-    uint8_t* act_q;               // W4A4:  codes [R][F/2]
-    uint8_t* act_s;               // W4A4:  scales [R][F/16]
-    float* Y;                     // fp32 [R][d]
+    uint16_t* act;                // SwiGLU output bf16 [R][F] (W4A4: exact dequantized NVFP4 values)
+    float* Y;                     // fp32 [R][d];  R = T*k + T
 };
 
 struct CombineArgs {
@@ -68,12 +65,15 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, hipStream_t s);
 hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 int gemm_bm(int path);            // rows per tile of the chosen path
 hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
+hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s);
+hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -57,6 +57,33 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     scales[b] = (uint8_t)sbyte;
 }
 
+// W4A4 activations: NVFP4 quantize-dequantize, one thread per 16-element block,
+// writing the exact dequantized values (code * scale) as bf16.
+__global__ __launch_bounds__(256) void fake_quant_act_kernel(const uint16_t* __restrict__ x, long long nblocks,
+                                                             uint16_t* __restrict__ out) {
+    long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + b * kBlock);
+    u32x4_t v0 = src[0], v1 = src[1];
+    uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    float bmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(f[i]));
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        o[i] = pack_hi16(nvfp4_fake_quant(f[2 * i], bmax), nvfp4_fake_quant(f[2 * i + 1], bmax));
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
+    dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+}
+
 __global__ void fill_zero_f32_kernel(float* p, int n) {
     int i = blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;
@@ -113,6 +140,13 @@ hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, 
     if (nb == 0) return hipSuccess;
     hipLaunchKernelGGL(quantize_blocks_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
                        C, 1, (const float*)nullptr, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, hipStream_t s) {
+    long long nb = (long long)R * (C / kBlock);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(fake_quant_act_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb, out);
     return hipGetLastError();
 }
 

@@ -112,19 +112,33 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // R2: certified top-k per token (one wave per token).
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxKS = 16;          // split-K slices of the logits GEMM
 constexpr int kSelWaves = 4;
 
 __device__ __forceinline__ double dot_f64(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g,
                                           int d, int lane) {
+    // fp64 products of bf16 pairs are exact; a lane sums its elements in a fixed
+    // order, then the wave reduces in a fixed tree.  Loads are issued 8 chunks at
+    // a time so one latency covers d = 4096.
     double s = 0.0;
-    for (int c = lane * 8; c < d; c += 512) {
-        u32x4_t vx = *reinterpret_cast<const u32x4_t*>(x + c);
-        u32x4_t vg = *reinterpret_cast<const u32x4_t*>(g + c);
-        uint32_t ax[4] = {vx.x, vx.y, vx.z, vx.w}, ag[4] = {vg.x, vg.y, vg.z, vg.w};
+    for (int c0 = lane * 8; c0 < d; c0 += 512 * 8) {
+        u32x4_t vx[8], vg[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s = fma((double)__uint_as_float(ax[q] << 16), (double)__uint_as_float(ag[q] << 16), s);
-            s = fma((double)__uint_as_float(ax[q] & 0xFFFF0000u), (double)__uint_as_float(ag[q] & 0xFFFF0000u), s);
+        for (int j = 0; j < 8; ++j) {
+            const int c = c0 + j * 512;
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            vx[j] = c < d ? *reinterpret_cast<const u32x4_t*>(x + c) : z;
+            vg[j] = c < d ? *reinterpret_cast<const u32x4_t*>(g + c) : z;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t ax[4] = {vx[j].x, vx[j].y, vx[j].z, vx[j].w};
+            const uint32_t ag[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s = fma((double)__uint_as_float(ax[q] << 16), (double)__uint_as_float(ag[q] << 16), s);
+                s = fma((double)__uint_as_float(ax[q] & 0xFFFF0000u), (double)__uint_as_float(ag[q] & 0xFFFF0000u), s);
+            }
         }
     }
     return wave_sum_f64(s);
@@ -159,36 +173,56 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
     int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ local_ids) {
+    // one workgroup per token: wave 0 bounds the logits and lists the candidates,
+    // all waves re-score candidates in fp64, wave 0 selects and normalises.
+    __shared__ int32_t s_cand[kMaxExperts];
+    __shared__ double s_score[kMaxExperts];
+    __shared__ int32_t s_ncand;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * kSelWaves + wave;
-    if (t >= T) return;                                   // wave-uniform
-    // bound factor gamma_n with n = d + KS additions, u' = 2^-23, plus a margin
-    const double u = 1.0 / 8388608.0;
-    const double n = (double)(d + KS);
-    const double gamma = n * u / (1.0 - n * u) * (1.0 + 1e-6);
-    const double tiny = (double)d * 1.1754943508222875e-38;   // d * 2^-126
-    double xs2 = 0.0;
-    for (int s = 0; s < KS; ++s) xs2 += xn2[(size_t)s * T + t];
-    const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
-    double lo[NS], hi[NS];
+    const int t = blockIdx.x;
+    const uint16_t* xrow = X + (size_t)t * d;
+    __shared__ double s_lo[kMaxExperts], s_hi[kMaxExperts];
+    {
+        // bounds for every expert, spread over the whole workgroup; the split-K
+        // partial sums are loaded together (KS <= kMaxKS) and added in slice order
+        const double u = 1.0 / 8388608.0;                  // bound factor gamma_n, n = d + KS, u' = 2^-23
+        const double n = (double)(d + KS);
+        const double gamma = n * u / (1.0 - n * u) * (1.0 + 1e-6);
+        const double tiny = (double)d * 1.1754943508222875e-38;   // d * 2^-126
+        double xv[kMaxKS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        int e = lane + 64 * i;
-        lo[i] = -INFINITY;
-        hi[i] = -INFINITY;
-        if (e < E) {
+        for (int s = 0; s < kMaxKS; ++s) xv[s] = s < KS ? xn2[(size_t)s * T + t] : 0.0;
+        double xs2 = 0.0;
+#pragma unroll
+        for (int s = 0; s < kMaxKS; ++s) xs2 += xv[s];
+        const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
+        for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
+            float pv[kMaxKS];
+            double gv[kMaxKS];
+#pragma unroll
+            for (int s = 0; s < kMaxKS; ++s) {
+                pv[s] = s < KS ? part[((size_t)s * T + t) * E + e] : 0.f;
+                gv[s] = s < KS ? gn2[(size_t)s * E + e] : 0.0;
+            }
             float lh = 0.f;
-            for (int s = 0; s < KS; ++s) lh += part[((size_t)s * T + t) * E + e];
             double gs2 = 0.0;
-            for (int s = 0; s < KS; ++s) gs2 += gn2[(size_t)s * E + e];
-            double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
-            lo[i] = (double)lh - beta;
-            hi[i] = (double)lh + beta;
+#pragma unroll
+            for (int s = 0; s < kMaxKS; ++s) { lh += pv[s]; gs2 += gv[s]; }
+            const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
+            s_lo[e] = (double)lh - beta;
+            s_hi[e] = (double)lh + beta;
         }
     }
-    // lowk = k-th largest lower bound
-    double lowk;
-    {
+    __syncthreads();
+    if (wave == 0) {
+        double lo[NS], hi[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int e = lane + 64 * i;
+            lo[i] = e < E ? s_lo[e] : -INFINITY;
+            hi[i] = e < E ? s_hi[e] : -INFINITY;
+        }
+        // lowk = k-th largest lower bound
         double tmp[NS];
 #pragma unroll
         for (int i = 0; i < NS; ++i) tmp[i] = lo[i];
@@ -199,50 +233,58 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
             for (int i = 0; i < NS; ++i)
                 if (lane + 64 * i == idx) tmp[i] = -INFINITY;
         }
-        // value of the k-th pick (broadcast from its owner)
         double v = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             if (lane + 64 * i == idx) v = lo[i];
-        lowk = __shfl(v, idx & 63, 64);
+        const double lowk = __shfl(v, idx & 63, 64);
+        // candidates (hi >= lowk), listed in increasing expert id
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const bool c = lane + 64 * i < E && hi[i] >= lowk;
+            const uint64_t m = __ballot(c);
+            if (c) s_cand[base + __popcll(m & ((1ull << lane) - 1ull))] = lane + 64 * i;
+            base += __popcll(m);
+        }
+        if (lane == 0) s_ncand = base;
     }
-    // candidates: hi >= lowk; re-score in fp64
+    __syncthreads();
+    const int nc = s_ncand;
+    for (int c = wave; c < nc; c += kSelWaves) {
+        const int e = s_cand[c];
+        const double sc = dot_f64(xrow, G + (size_t)e * d, d, lane);
+        if (lane == 0) s_score[c] = sc;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // top-k among candidates by (fp64 score desc, id asc): candidate slots c = lane + 64 i
     double sc[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) sc[i] = -INFINITY;
-    const uint16_t* xrow = X + (size_t)t * d;
-#pragma unroll
     for (int i = 0; i < NS; ++i) {
-        uint64_t m = __ballot(lane + 64 * i < E && hi[i] >= lowk);
-        while (m) {
-            int b = __builtin_ctzll(m);
-            m &= m - 1;
-            int e = b + 64 * i;
-            double s = dot_f64(xrow, G + (size_t)e * d, d, lane);
-            if (lane == b) sc[i] = s;
-        }
+        const int c = lane + 64 * i;
+        sc[i] = c < nc ? s_score[c] : -INFINITY;
     }
-    // top-k among candidates by (fp64 score desc, id asc)
     int my_id = -1;
     double my_score = 0.0, top_score = 0.0;
     for (int r = 0; r < topk; ++r) {
-        int idx = wave_argmax<NS>(sc, E, lane);
+        const int idx = wave_argmax<NS>(sc, nc, lane);
         double v = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             if (lane + 64 * i == idx) { v = sc[i]; sc[i] = -INFINITY; }
         v = __shfl(v, idx & 63, 64);    // broadcast from the owner lane
         if (r == 0) top_score = v;
-        if (lane == r) { my_id = idx; my_score = v; }
+        if (lane == r) { my_id = s_cand[idx]; my_score = v; }
     }
     // softmax over the k selected fp64 scores
-    double z = lane < topk ? exp(my_score - top_score) : 0.0;
-    double zs = wave_sum_f64(z);
+    const double z = lane < topk ? exp(my_score - top_score) : 0.0;
+    const double zs = wave_sum_f64(z);
     if (lane < topk) {
-        size_t o = (size_t)t * topk + lane;
+        const size_t o = (size_t)t * topk + lane;
         topk_ids[o] = my_id;
         topk_w[o] = (float)(z / zs);
-        int lam = my_id - offset;
+        const int lam = my_id - offset;
         local_ids[o] = (lam >= 0 && lam < L) ? lam : -1;
     }
 }
@@ -293,13 +335,54 @@ __global__ __launch_bounds__(kPermBlock) void perm_block_kernel(
 // tile.  Groups 0..L-1 are the local experts (rows [offsets[g], offsets[g+1])
 // of the permuted-pair row space), group L the shared expert (rows [Tk, Tk+T)).
 // ---------------------------------------------------------------------------
+// Block-wide exclusive scans of (count, tiles) over 1024 threads (one per expert),
+// then the tile table: rows [offsets[g], offsets[g+1]) of expert g in BM-row
+// tiles, followed by the shared expert's rows [Tk, Tk+T).
+__device__ void scan_and_emit_tiles(int c, int L, int T, int topk, int has_shared, int BM,
+                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                    int4* __restrict__ tiles, int32_t* __restrict__ ntiles, int max_tiles,
+                                    int32_t* s_off) {
+    __shared__ int32_t s_wsum[16], s_wsum_t[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tc = tid < L ? (c + BM - 1) / BM : 0;
+    int ic = c, it = tc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int vc = __shfl_up(ic, o, 64), vt = __shfl_up(it, o, 64);
+        if (lane >= o) { ic += vc; it += vt; }
+    }
+    if (lane == 63) { s_wsum[wave] = ic; s_wsum_t[wave] = it; }
+    __syncthreads();
+    int basec = 0, baset = 0;
+    for (int w = 0; w < wave; ++w) { basec += s_wsum[w]; baset += s_wsum_t[w]; }
+    const int exc = basec + ic - c, ext = baset + it - tc;
+    if (tid < L) {
+        counts[tid] = c;
+        offsets[tid] = exc;
+        if (s_off) s_off[tid] = exc;
+        for (int i = 0; i < tc; ++i) {
+            const int rb = exc + i * BM;
+            tiles[ext + i] = make_int4(tid, rb, min(rb + BM, exc + c), 0);
+        }
+    }
+    if (tid == L - 1) {
+        offsets[L] = exc + c;
+        int n = ext + tc;
+        if (has_shared) {
+            const int base = T * topk;
+            const int st = (T + BM - 1) / BM;
+            for (int i = 0; i < st; ++i)
+                tiles[n + i] = make_int4(L, base + i * BM, min(base + (i + 1) * BM, base + T), 0);
+            n += st;
+        }
+        ntiles[0] = n < max_tiles ? n : max_tiles;
+    }
+}
+
 __global__ __launch_bounds__(1024) void perm_scan_kernel(
     int32_t* __restrict__ block_counts, int nblk, int L, int T, int topk, int has_shared, int BM,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
     int32_t* __restrict__ ntiles, int max_tiles) {
-    __shared__ int32_t s_cnt[1024];
-    __shared__ int32_t s_tiles[1024];
-    __shared__ int32_t s_wsum[16];
     const int tid = threadIdx.x;
     // per-expert scan over blocks (L <= 1024: one thread per expert)
     int total = 0;
@@ -309,44 +392,44 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
             block_counts[(size_t)b * L + tid] = total;
             total += c;
         }
-        counts[tid] = total;
     }
-    s_cnt[tid] = tid < L ? total : 0;
-    s_tiles[tid] = tid < L ? (total + BM - 1) / BM : 0;
+    scan_and_emit_tiles(total, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, nullptr);
+}
+
+// All three permutation steps in one workgroup, for T <= kPermBlock.
+__global__ __launch_bounds__(1024) void perm_small_kernel(
+    const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared, int BM,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
+    int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    extern __shared__ uint32_t masks[];                    // [L][kPermBlock/32]
+    __shared__ int32_t s_off[1024];
+    constexpr int W = kPermBlock / 32;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < L * W; i += 1024) masks[i] = 0u;
     __syncthreads();
-    // block-wide exclusive scans of counts and tile counts (wave scans + wave sums)
-    const int lane = tid & 63, wave = tid >> 6;
-    int c = s_cnt[tid], tc = s_tiles[tid];
-    int ic = c, it = tc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int vc = __shfl_up(ic, o, 64), vt = __shfl_up(it, o, 64);
-        if (lane >= o) { ic += vc; it += vt; }
-    }
-    __shared__ int32_t s_wsum_t[16];
-    if (lane == 63) { s_wsum[wave] = ic; s_wsum_t[wave] = it; }
+    if (tid < T)
+        for (int j = 0; j < topk; ++j) {
+            const int lam = local_ids[(size_t)tid * topk + j];
+            if (lam >= 0) atomicOr(&masks[lam * W + (tid >> 5)], 1u << (tid & 31));
+        }
     __syncthreads();
-    int basec = 0, baset = 0;
-    for (int w = 0; w < wave; ++w) { basec += s_wsum[w]; baset += s_wsum_t[w]; }
-    int exc = basec + ic - c, ext = baset + it - tc;
-    if (tid < L) offsets[tid] = exc;
-    if (tid == L - 1) offsets[L] = exc + c;
-    if (tid < L) {
-        for (int i = 0; i < tc; ++i) {
-            int rb = exc + i * BM;
-            tiles[ext + i] = make_int4(tid, rb, min(rb + BM, exc + c), 0);
+    int c = 0;
+    if (tid < L)
+        for (int w = 0; w < W; ++w) c += __popc(masks[tid * W + w]);
+    scan_and_emit_tiles(c, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, s_off);
+    __syncthreads();
+    for (int p = tid; p < T * topk; p += 1024) {
+        const int t = p / topk;
+        const int lam = local_ids[p];
+        int pos = -1;
+        if (lam >= 0) {
+            int r = 0;
+            for (int w = 0; w < (t >> 5); ++w) r += __popc(masks[lam * W + w]);
+            r += __popc(masks[lam * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
+            pos = s_off[lam] + r;
+            perm[pos] = p;
         }
-    }
-    if (tid == L - 1) {
-        int n = ext + tc;
-        if (has_shared) {
-            int base = T * topk;
-            int st = (T + BM - 1) / BM;
-            for (int i = 0; i < st; ++i)
-                tiles[n + i] = make_int4(L, base + i * BM, min(base + (i + 1) * BM, base + T), 0);
-            n += st;
-        }
-        ntiles[0] = n < max_tiles ? n : max_tiles;
+        inv[p] = pos;
     }
 }
 
@@ -378,6 +461,7 @@ int router_ksplit(int T, int E, int d) {
     if (base < 1) return 1;                      // empty batch
     int ks = (512 + base - 1) / base;
     int maxks = d / 256 > 0 ? d / 256 : 1;
+    if (maxks > kMaxKS) maxks = kMaxKS;
     if (ks > maxks) ks = maxks;
     if (ks < 1) ks = 1;
     return ks;
@@ -389,7 +473,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     dim3 g1((a.T + kR1Tile - 1) / kR1Tile, (a.E + kR1Tile - 1) / kR1Tile, KS);
     hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
                        a.part, a.xn2, a.gn2);
-    dim3 g2((a.T + kSelWaves - 1) / kSelWaves);
+    dim3 g2(a.T);
     const int ns = (a.E + 63) / 64;
 #define SEL(NSV)                                                                                       \
     hipLaunchKernelGGL(router_select_kernel<NSV>, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, \
@@ -409,6 +493,12 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
 hipError_t launch_permute(const PermArgs& a, hipStream_t s) {
     const int nblk = (a.T + kPermBlock - 1) / kPermBlock;
     const size_t lds = (size_t)a.L * (kPermBlock / 32) * sizeof(uint32_t);
+    if (nblk <= 1) {
+        hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), lds, s, a.local_ids, a.T, a.topk, a.L,
+                           a.has_shared, a.BM, a.counts, a.offsets, a.tiles, a.ntiles, a.max_tiles, a.perm,
+                           a.inv);
+        return hipGetLastError();
+    }
     if (nblk > 0)
         hipLaunchKernelGGL(perm_block_kernel, dim3(nblk), dim3(kPermBlock), lds, s, a.local_ids, a.T,
                            a.topk, a.L, a.block_counts, a.rank);
