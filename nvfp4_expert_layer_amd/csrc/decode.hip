@@ -2,24 +2,27 @@
 //
 // When each expert sees only a few tokens (decode, or a shard's share of a small
 // batch) the layer is bound by streaming the NVFP4 weights from HBM once.  Each
-// wave owns 16 weight rows, loads 32 contiguous code bytes per lane per step with
-// a two-step register prefetch, and the workgroup's waves share the token rows
-// through LDS, staged in double-buffered 512-element K chunks.
+// wave owns 16 weight rows at a time, loads 32 contiguous code bytes per lane per
+// step with a register prefetch ring DEPTH steps deep, and walks RGS row groups
+// back to back so the ring never drains between them.  The workgroup's waves
+// share the token rows through LDS: the whole K range when it fits, else
+// double-buffered 512-element chunks.
 //
 // Block-diagonal MFMA (v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8 k] and
 // B[8 k][l%16]; D[4 rows][l%16]).  The reduction index is a free permutation:
 // K is cut into chunks of 64 elements (32 code bytes, 4 E4M3 scale bytes); at
 // step i lane group g = l/16 takes chunk 4i + g, so the four lanes of a weight
-// row read one whole 128-byte line per step.  B = the codes decoded UNSCALED to bf16 (v_cvt_scalef32_pk_bf16_fp4
-// with scale 1: exact, one instruction per two codes).  A row m = 4 j + t holds
-// token t of the current group of four, restricted to the K elements of lane
-// group j (zero elsewhere).  An MFMA pair over 16 consecutive elements of the
-// chunk then yields, in lane group j, the four tokens' partial dot products
-// over exactly one 16-element block of row n -- the block whose E4M3 scale that
-// lane already holds -- so the scale is applied with one fp32 FMA per output.
-// After the K loop the four lane groups are summed (two xor-shuffles) and the
-// fp32 global scale is applied.  Cost: ~0.8 VALU op per weight element for four
-// tokens, against ~2 for dequantize-then-MFMA.
+// row read one whole 128-byte line per step.  B = the codes decoded UNSCALED to
+// bf16 (v_cvt_scalef32_pk_bf16_fp4 with scale 1: exact, one instruction per two
+// codes).  A row m = 4 j + t holds token t of the current group of four,
+// restricted to the K elements of lane group j (zero elsewhere).  An MFMA pair
+// over 16 consecutive elements of the chunk then yields, in lane group j, the
+// four tokens' partial dot products over exactly one 16-element block of row n
+// -- the block whose E4M3 scale that lane already holds -- so the scale is
+// applied with one fp32 FMA per output.  After the K loop the four lane groups
+// are summed (two xor-shuffles) and the fp32 global scale is applied.  Cost:
+// ~0.8 VALU op per weight element for four tokens, against ~2 for
+// dequantize-then-MFMA.
 //
 // GEMM1 epilogue: a = silu(gate) * up (rows [0,F) of w13 gate, [F,2F) up), bf16;
 // W4A4 quantize-dequantizes a per 16 columns.  GEMM2: Y = acc * g2 (fp32 rows).
@@ -31,162 +34,239 @@
 
 namespace moe {
 
-constexpr int kDecWaves = 4;        // waves per workgroup, 16 weight rows each
-constexpr int kDecRows = 16;        // token rows per tile (four groups of four)
-constexpr int kChunk = 512;         // K elements per LDS chunk (4 steps of 128)
+constexpr int kDecWaves = 4;        // waves per workgroup, 16 weight rows each at a time
+constexpr int kChunk = 512;         // K elements per LDS chunk when A is staged in chunks
 constexpr int kAPad = 8;            // bf16 padding per LDS row
-constexpr int kLdsElems = 2 * kDecRows * (kChunk + kAPad);
+constexpr int kFullALds = 65536;    // largest whole-K A stage (bytes)
 
-__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
-    return *reinterpret_cast<const uint16_t*>(p);
+// LDS bytes of the A stage: whole K, or two chunks.
+__host__ __device__ constexpr int dec_lds_bytes(int rows, int K, bool full) {
+    return full ? rows * (K + kAPad) * 2 : 2 * rows * (kChunk + kAPad) * 2;
 }
 
-// Streams K for NR weight-row groups (16 rows each) against the tile's token
-// rows.  codes[r]/scales[r]: this lane's row at its first chunk.  arows: the
-// tile's token rows (bf16, K long), ntok of them valid.  Leaves per lane, for
-// each of the 4 token groups, the 4 tokens' sums over this lane group's K share.
+// Streams RGS x K for NR weight-row groups (16 rows each) against the tile's
+// token rows (at most 4 * TGM, in TGM groups of four).
+//   codes[r] / scales[r]: start of this lane's row of row group r;
+//   cstride / sstride: bytes to the same lane's row in the next sequential row group;
+//   arows: the tile's token rows (bf16, K long), ntok of them valid;
+//   epi(j, acc): called after sequential row group j with, per token group, the
+//   four tokens' sums over this lane group's K share.
 // A step covers 256 elements of K: lane group g takes the 64-element chunk
-// 4 i + g (32 code bytes, 4 scale bytes); chunks past K (K % 256 == 128) are
-// skipped by the two upper lane groups.
-template <int NR>
+// 4 i + g; chunks past K (K % 256 == 128) are skipped by the upper lane groups.
+template <int NR, int TGM, int DEPTH, int RGS, bool FULLA, bool SEG, class Epi>
 __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ arows, int ntok, int K,
                                            const uint8_t* const (&codes)[NR],
-                                           const uint8_t* const (&scales)[NR], uint16_t* lds,
-                                           f32x4_t (&acc)[4][NR]) {
+                                           const uint8_t* const (&scales)[NR], size_t cstride,
+                                           size_t sstride, uint16_t* lds, Epi epi) {
+    constexpr int ROWS = 4 * TGM;
+    static_assert(FULLA || RGS == 1, "chunked A stages serve one row group");
+    static_assert(!SEG || DEPTH % 4 == 0, "scale segments cover four steps");
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
     const int ntg = (ntok + 3) >> 2;
-    const int nsteps = (K + 255) / 256, nchunks = (K + kChunk - 1) / kChunk;   // K % 128 == 0
-    constexpr int LDW = kChunk + kAPad;                      // LDS row stride (elements)
+    const int nsteps = (K + 255) / 256;                      // K % 128 == 0
+    const int nvirt = RGS * nsteps;
+    const int LDW = FULLA ? K + kAPad : kChunk + kAPad;      // LDS row stride (elements)
     uint16_t* const buf0 = lds;
-    uint16_t* const buf1 = lds + kDecRows * LDW;
+    uint16_t* const buf1 = lds + ROWS * LDW;
+
+    // ---- A stage: whole K once, or chunk 0 (the rest double-buffered below)
+    constexpr int APT = ROWS * (kChunk / 8) / (64 * kDecWaves);   // 16-byte pieces per thread per chunk
+    static_assert(APT * 64 * kDecWaves == ROWS * kChunk / 8, "A staging covers the chunk");
+    u32x4_t va[APT];
+    auto a_load = [&](int ch) {
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg)
+        for (int j = 0; j < APT; ++j) {
+            const int piece = tid + j * (64 * kDecWaves);
+            const int row = piece >> 6, col = ch * kChunk + (piece & 63) * 8;
+            if (row < ntok && col < K) va[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + col);
+        }
+    };
+    auto a_store = [&](int ch, uint16_t* b) {
+#pragma unroll
+        for (int j = 0; j < APT; ++j) {
+            const int piece = tid + j * (64 * kDecWaves);
+            const int row = piece >> 6, colc = (piece & 63) * 8, col = ch * kChunk + colc;
+            if (row < ntok && col < K) *reinterpret_cast<u32x4_t*>(b + row * LDW + (FULLA ? col : colc)) = va[j];
+        }
+    };
+
+    // ---- weight prefetch ring.  Loads are unconditional and never selected on:
+    // a prefetch past the last step re-reads the last step, and a chunk past K
+    // (K % 256 == 128) reads the last chunk of K -- both lines were just fetched,
+    // and such data is either unused or multiplied by a zero A fragment.  This
+    // lets the compiler keep DEPTH steps of loads in flight across the loop.
+    const int last_chunk = K / 64 - 1;
+    auto load_codes = [&](int r, int v, u32x4_t& lo, u32x4_t& hi, uint32_t& sc) {
+        const int vv = v < nvirt ? v : nvirt - 1;
+        const int j = vv / nsteps, step = vv - j * nsteps;
+        const int chunk = min(step * 4 + g, last_chunk);
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(codes[r] + j * cstride + (size_t)chunk * 32);
+        lo = p[0];
+        hi = p[1];
+        if (!SEG) sc = *reinterpret_cast<const uint32_t*>(scales[r] + j * sstride + (size_t)chunk * 4);
+    };
+    // SEG: scales come in 16-byte segments, one per step (the four lane groups'
+    // chunks); lane group m loads the segment of step 4G + m of group G (64
+    // adjacent bytes per row), and a 4x4 transpose across lane groups (two
+    // permlane32 and two permlane16 swaps) leaves in lane group g, register m,
+    // the 4 scale bytes of its own chunk at step 4G + m.  Needs K % 1024 == 0.
+    auto load_seg = [&](int r, int grp) -> u32x4_t {
+        int v = grp * 4 + g;
+        v = v < nvirt ? v : nvirt - 1;
+        const int j = v / nsteps, step = v - j * nsteps;
+        return *reinterpret_cast<const u32x4_t*>(scales[r] + j * sstride + (size_t)step * 16);
+    };
+    auto transpose4 = [](u32x4_t x) -> u32x4_t {
+        unsigned r0 = x.x, r1 = x.y, r2 = x.z, r3 = x.w;
+        auto p = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+        r0 = p[0];
+        r2 = p[1];
+        p = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+        r1 = p[0];
+        r3 = p[1];
+        p = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+        r0 = p[0];
+        r1 = p[1];
+        p = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
+        r2 = p[0];
+        r3 = p[1];
+        return u32x4_t{r0, r1, r2, r3};
+    };
+    u32x4_t seg_next[NR], seg_cur[NR];
+    if (SEG) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            seg_cur[r] = transpose4(load_seg(r, 0));
+            seg_next[r] = load_seg(r, 1);
+        }
+    }
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+    u32x4_t wl[DEPTH][NR], wh[DEPTH][NR];
+    uint32_t ws[DEPTH][NR];
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) load_codes(r, u, wl[u][r], wh[u][r], ws[u][r]);
+
+    if (FULLA) {
+        const int nch = (K + kChunk - 1) / kChunk;
+        for (int ch = 0; ch < nch; ++ch) {
+            a_load(ch);
+            a_store(ch, buf0);
+        }
+        __syncthreads();
+    } else {
+        a_load(0);
+        a_store(0, buf0);
+    }
+
+    f32x4_t acc[TGM][NR];
+#pragma unroll
+    for (int tg = 0; tg < TGM; ++tg)
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc[tg][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // A staging: 16 rows x 512 elements = 1024 pieces of 16 bytes, 4 per thread;
-    // rows >= ntok are neither loaded nor read.
-    static_assert(64 * kDecWaves * 4 == kDecRows * kChunk / 8, "A staging covers the chunk");
-    u32x4_t va[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int piece = tid + j * (64 * kDecWaves);
-        const int row = piece >> 6, col = (piece & 63) * 8;
-        if (row < ntok && col < K) {
-            va[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + col);
-            *reinterpret_cast<u32x4_t*>(buf0 + row * LDW + col) = va[j];
-        }
-    }
-
-    // weight prefetch, two steps ahead (32 code bytes + 4 scale bytes per step)
-    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-    auto load_codes = [&](int r, int step, u32x4_t& lo, u32x4_t& hi, uint32_t& sc) {
-        if ((step * 4 + g) * 64 < K) {
-            const u32x4_t* p = reinterpret_cast<const u32x4_t*>(codes[r] + (size_t)step * 128);
-            lo = p[0];
-            hi = p[1];
-            sc = *reinterpret_cast<const uint32_t*>(scales[r] + (size_t)step * 16);
-        } else {
-            lo = zero4;
-            hi = zero4;
-            sc = 0u;
-        }
-    };
-    u32x4_t c0l[NR], c0h[NR], c1l[NR], c1h[NR];
-    uint32_t s0[NR], s1[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        load_codes(r, 0, c0l[r], c0h[r], s0[r]);
-        c1l[r] = zero4; c1h[r] = zero4; s1[r] = 0u;
-        if (nsteps > 1) load_codes(r, 1, c1l[r], c1h[r], s1[r]);
-    }
     // block-diagonal ownership: A row m = 4 j + t is non-zero only in lane group j
     const bool aown = (n >> 2) == g;
     const int tsub = n & 3;
+    constexpr int SPC = kChunk / 256;                        // steps per LDS chunk
+    static_assert(FULLA || DEPTH % SPC == 0, "ring aligned with LDS chunks");
 
-    for (int ch = 0; ch < nchunks; ++ch) {
-        __syncthreads();                                     // chunk ch staged, chunk ch-1 consumed
-        const bool more = ch + 1 < nchunks;
-        if (more) {
+    auto do_step = [&](const int u, const int v) {
+        const int j = v / nsteps, step = v - j * nsteps;
+        const int ch = step / SPC, si = step % SPC;
+        if (!FULLA && si == 0) {
+            __syncthreads();                                 // chunk ch staged, chunk ch-1 consumed
+            if ((ch + 1) * kChunk < K) a_load(ch + 1);
+        }
+        const uint16_t* ab = FULLA ? buf0 : ((ch & 1) ? buf1 : buf0);
+        u32x4_t cl[NR], chh[NR];
+        uint32_t sc[NR];
+        if (SEG && u % 4 == 0 && v > 0) {
+            // next group of four steps: its segment arrived long ago; fetch the one after
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int piece = tid + j * (64 * kDecWaves);
-                const int row = piece >> 6, col = (piece & 63) * 8;
-                if (row < ntok && (ch + 1) * kChunk + col < K)
-                    va[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + (ch + 1) * kChunk + col);
+            for (int r = 0; r < NR; ++r) {
+                seg_cur[r] = transpose4(seg_next[r]);
+                seg_next[r] = load_seg(r, v / 4 + 1);
             }
         }
-        const uint16_t* ab = (ch & 1) ? buf1 : buf0;
 #pragma unroll
-        for (int si = 0; si < kChunk / 256; ++si) {
-            const int step = ch * (kChunk / 256) + si;
-            if (step >= nsteps) break;                       // last chunk may hold fewer steps
-            u32x4_t cl[NR], chh[NR];
-            uint32_t sc[NR];
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                cl[r] = c0l[r]; chh[r] = c0h[r]; sc[r] = s0[r];
-                c0l[r] = c1l[r]; c0h[r] = c1h[r]; s0[r] = s1[r];
+        for (int r = 0; r < NR; ++r) {
+            cl[r] = wl[u][r];
+            chh[r] = wh[u][r];
+            if (SEG) {
+                const u32x4_t sgc = seg_cur[r];
+                sc[r] = (u % 4 == 0) ? sgc.x : (u % 4 == 1) ? sgc.y : (u % 4 == 2) ? sgc.z : sgc.w;
+            } else {
+                sc[r] = ws[u][r];
             }
-            if (step + 2 < nsteps) {
+        }
+        const bool kvalid = (step * 4 + g) * 64 < K;
+        const int kcol = FULLA ? (step * 4 + g) * 64 : (si * 4 + g) * 64;
 #pragma unroll
-                for (int r = 0; r < NR; ++r) load_codes(r, step + 2, c1l[r], c1h[r], s1[r]);
-            }
-            const bool kvalid = (step * 4 + g) * 64 < K;
-            const int kcol = (si * 4 + g) * 64;              // this lane group's chunk inside the LDS chunk
+        for (int r = 0; r < NR; ++r) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) {
+            for (int h = 0; h < 2; ++h) {
+                // 32 of the chunk's 64 elements: two 16-element blocks
+                const u32x4_t c = h ? chh[r] : cl[r];
+                bf16x8_t b[4];
+                b[0] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.x));
+                b[1] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.y));
+                b[2] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.z));
+                b[3] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.w));
+                const float sa = e4m3_to_f32((sc[r] >> (16 * h)) & 0xFFu);
+                const float sb = e4m3_to_f32((sc[r] >> (16 * h + 8)) & 0xFFu);
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    // 32 of the chunk's 64 elements: two 16-element blocks
-                    const u32x4_t c = h ? chh[r] : cl[r];
-                    bf16x8_t b[4];
-                    b[0] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.x));
-                    b[1] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.y));
-                    b[2] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.z));
-                    b[3] = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16(c.w));
-                    const float sa = e4m3_to_f32((sc[r] >> (16 * h)) & 0xFFu);
-                    const float sb = e4m3_to_f32((sc[r] >> (16 * h + 8)) & 0xFFu);
+                for (int tg = 0; tg < TGM; ++tg) {
+                    if (tg < ntg) {
+                        u32x4_t av[4];
 #pragma unroll
-                    for (int tg = 0; tg < 4; ++tg) {
-                        if (tg < ntg) {
-                            u32x4_t av[4];
+                        for (int q = 0; q < 4; ++q) av[q] = zero4;
+                        const int tok = tg * 4 + tsub;
+                        if (aown && kvalid && tok < ntok) {
+                            const uint16_t* p = ab + tok * LDW + kcol + h * 32;
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) av[q] = zero4;
-                            const int tok = tg * 4 + tsub;
-                            if (aown && kvalid && tok < ntok) {
-                                const uint16_t* p = ab + tok * LDW + kcol + h * 32;
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) av[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
-                            }
-                            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                            f32x4_t da = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, av[0]), b[0], z, 0, 0, 0);
-                            da = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[1]),
-                                                                         b[1], da, 0, 0, 0);
-                            f32x4_t db = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, av[2]), b[2], z, 0, 0, 0);
-                            db = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[3]),
-                                                                         b[3], db, 0, 0, 0);
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                acc[tg][r][q] = fmaf(sb, db[q], fmaf(sa, da[q], acc[tg][r][q]));
+                            for (int q = 0; q < 4; ++q) av[q] = *reinterpret_cast<const u32x4_t*>(p + q * 8);
                         }
+                        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                        f32x4_t da = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, av[0]), b[0], z, 0, 0, 0);
+                        da = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[1]), b[1],
+                                                                     da, 0, 0, 0);
+                        f32x4_t db = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, av[2]), b[2], z, 0, 0, 0);
+                        db = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[3]), b[3],
+                                                                     db, 0, 0, 0);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[tg][r][q] = fmaf(sb, db[q], fmaf(sa, da[q], acc[tg][r][q]));
                     }
                 }
             }
         }
-        if (more) {
-            uint16_t* nb = (ch & 1) ? buf0 : buf1;
+        // refill this ring slot only after its last use: the new load then takes
+        // over the same registers and no copies of in-flight data are needed
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int piece = tid + j * (64 * kDecWaves);
-                const int row = piece >> 6, col = (piece & 63) * 8;
-                if (row < ntok && (ch + 1) * kChunk + col < K) *reinterpret_cast<u32x4_t*>(nb + row * LDW + col) = va[j];
-            }
+        for (int r = 0; r < NR; ++r) load_codes(r, v + DEPTH, wl[u][r], wh[u][r], ws[u][r]);
+        if (!FULLA && si == SPC - 1 && (ch + 1) * kChunk < K) a_store(ch + 1, (ch & 1) ? buf0 : buf1);
+        if (step == nsteps - 1) {
+            epi(j, acc);
+#pragma unroll
+            for (int tg = 0; tg < TGM; ++tg)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) acc[tg][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
+    };
+    // whole ring rounds without bounds checks, then the tail
+    int v0 = 0;
+    for (; v0 + DEPTH <= nvirt; v0 += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) do_step(u, v0 + u);
     }
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+        if (v0 + u < nvirt) do_step(u, v0 + u);
 }
 
 // Sum of a value over the four lane groups (lanes l, l^16, l^32, l^48).
@@ -196,9 +276,21 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
-// Tile set-up shared by both GEMMs.
+// Token-group sum of row group r for token 4 tg + g (every lane takes part in
+// the shuffles; lane group g keeps its own token).
+template <int TGM, int NR>
+__device__ __forceinline__ float dec_result(const f32x4_t (&acc)[TGM][NR], int tg, int r, int g) {
+    float out = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float v = lane_group_sum(acc[tg][r][q]);
+        if (q == g) out = v;
+    }
+    return out;
+}
+
 struct DecTile {
-    int grp, rb, re;
+    int rb, re;
     bool shared;
     size_t ex;
 };
@@ -206,7 +298,6 @@ struct DecTile {
 __device__ __forceinline__ DecTile dec_tile(const GemmArgs& a) {
     const int4 tl = a.tiles[blockIdx.x];
     DecTile t;
-    t.grp = tl.x;
     t.rb = tl.y;
     t.re = tl.z;
     t.shared = tl.x == a.L;
@@ -215,23 +306,29 @@ __device__ __forceinline__ DecTile dec_tile(const GemmArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM1 + SwiGLU: a wave = 16 SwiGLU columns (16 gate + 16 up rows of w13) for a
-// tile of <= 16 token rows.  grid (max_tiles, F / (16 * kDecWaves)).
+// GEMM1 + SwiGLU: a workgroup = 32 SwiGLU columns of a tile of <= 4 TGM token
+// rows; waves 0,1 stream the gate rows of columns [c0, c0+16) and [c0+16, c0+32),
+// waves 2,3 the matching up rows; the up results meet the gate results in LDS.
+// grid (max_tiles, F / 32).
 // ---------------------------------------------------------------------------
-template <int MODE>
-__global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(3))) void dec_gemm1_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
-    __shared__ const uint16_t* s_arow[kDecRows];
+template <int MODE, int TGM, int DEPTH, bool FULLA, bool SEG>
+__global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
+    constexpr int ROWS = 4 * TGM;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ const uint16_t* s_arow[ROWS];
+    __shared__ float s_up[2][TGM][64];
     if ((int)blockIdx.x >= *a.ntiles) return;
     const DecTile tl = dec_tile(a);
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
     const int d = a.d, F = a.F;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col0 = (blockIdx.y * kDecWaves + wave) * 16;
+    const int half = wave & 1;                       // which 16 columns
+    const bool is_up = wave >= 2;
+    const int col0 = blockIdx.y * 32 + half * 16;
     const int n = lane & 15, g = lane >> 4;
     const int ntok = tl.re - tl.rb;
     const uint16_t* act_in = MODE == 0 ? a.hidden : a.hq;
-    if (tid < kDecRows) {
+    if (tid < ROWS) {
         const int row = tl.rb + tid;
         int t = 0;
         if (row < tl.re) t = tl.shared ? row - a.T * a.topk : a.perm[row] / a.topk;
@@ -240,87 +337,136 @@ __global__ __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     const uint8_t* w13 = W.w13 + tl.ex * (size_t)(2 * F) * (d / 2);
     const uint8_t* w13s = W.w13_s + tl.ex * (size_t)(2 * F) * (d / 16);
-    const uint8_t* const codes[2] = {w13 + (size_t)(col0 + n) * (d / 2) + g * 32,
-                                     w13 + (size_t)(F + col0 + n) * (d / 2) + g * 32};
-    const uint8_t* const scales[2] = {w13s + (size_t)(col0 + n) * (d / 16) + g * 4,
-                                      w13s + (size_t)(F + col0 + n) * (d / 16) + g * 4};
-    f32x4_t acc[4][2];
-    dec_stream<2>(s_arow, ntok, d, codes, scales, lds, acc);
-
+    const int wrow = (is_up ? F : 0) + col0 + n;
+    const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2)};
+    const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16)};
     const float g13 = W.g13[tl.ex];
     const int col = col0 + n;
+    auto epi = [&](int, const f32x4_t (&acc)[TGM][1]) {
+        float v[TGM];
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-        // every lane group joins the shuffles; lane group g keeps token 4 tg + g
-        float gt = 0.f, up = 0.f;
+        for (int tg = 0; tg < TGM; ++tg) v[tg] = dec_result<TGM, 1>(acc, tg, 0, g) * g13;
+        if (is_up) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float sgt = lane_group_sum(acc[tg][0][q]), sup = lane_group_sum(acc[tg][1][q]);
-            if (q == g) { gt = sgt; up = sup; }
+            for (int tg = 0; tg < TGM; ++tg) s_up[half][tg][lane] = v[tg];
         }
-        gt *= g13;
-        up *= g13;
-        float av = gt / (1.0f + expf(-gt)) * up;
-        if (MODE == 1) {
-            // NVFP4 quantize-dequantize over the 16 columns of this lane group
-            float m = fabsf(av);
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            m = fmaxf(m, __shfl_xor(m, 2, 64));
-            m = fmaxf(m, __shfl_xor(m, 4, 64));
-            m = fmaxf(m, __shfl_xor(m, 8, 64));
-            av = nvfp4_fake_quant(av, m);
+        __syncthreads();
+        if (!is_up) {
+#pragma unroll
+            for (int tg = 0; tg < TGM; ++tg) {
+                const float gt = v[tg], up = s_up[half][tg][lane];
+                float av = gt / (1.0f + expf(-gt)) * up;
+                if (MODE == 1) {
+                    // NVFP4 quantize-dequantize over the 16 columns of this lane group
+                    float m = fabsf(av);
+                    m = fmaxf(m, __shfl_xor(m, 1, 64));
+                    m = fmaxf(m, __shfl_xor(m, 2, 64));
+                    m = fmaxf(m, __shfl_xor(m, 4, 64));
+                    m = fmaxf(m, __shfl_xor(m, 8, 64));
+                    av = nvfp4_fake_quant(av, m);
+                }
+                const int r = tl.rb + tg * 4 + g;
+                if (r < tl.re) a.act[(size_t)r * F + col] = (uint16_t)f32_to_bf16_rne(av);
+            }
         }
-        const int r = tl.rb + tg * 4 + g;
-        if (r < tl.re) a.act[(size_t)r * F + col] = (uint16_t)f32_to_bf16_rne(av);
-    }
+    };
+    dec_stream<1, TGM, DEPTH, 1, FULLA, SEG>(s_arow, ntok, d, codes, scales, 0, 0, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
-// GEMM2: a wave = 16 output columns (16 rows of w2).  grid (max_tiles, d / 64).
+// GEMM2: a wave walks RGS groups of 16 output columns (16 rows of w2 each); the
+// workgroup covers 16 * kDecWaves * RGS columns.  grid (max_tiles, d / that).
 // ---------------------------------------------------------------------------
+template <int TGM, int DEPTH, int RGS, bool FULLA, bool SEG>
 __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
-    __shared__ const uint16_t* s_arow[kDecRows];
+    constexpr int ROWS = 4 * TGM;
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ const uint16_t* s_arow[ROWS];
     if ((int)blockIdx.x >= *a.ntiles) return;
     const DecTile tl = dec_tile(a);
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
     const int d = a.d, F = a.F;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col0 = (blockIdx.y * kDecWaves + wave) * 16;
+    const int cbase = blockIdx.y * (16 * kDecWaves * RGS) + wave * 16;   // row group j: cbase + 64 j
     const int n = lane & 15, g = lane >> 4;
     const int ntok = tl.re - tl.rb;
-    if (tid < kDecRows) s_arow[tid] = a.act + (size_t)(tl.rb + (tid < ntok ? tid : 0)) * F;
+    if (tid < ROWS) s_arow[tid] = a.act + (size_t)(tl.rb + (tid < ntok ? tid : 0)) * F;
     __syncthreads();
     const uint8_t* w2 = W.w2 + tl.ex * (size_t)d * (F / 2);
     const uint8_t* w2s = W.w2_s + tl.ex * (size_t)d * (F / 16);
-    const uint8_t* const codes[1] = {w2 + (size_t)(col0 + n) * (F / 2) + g * 32};
-    const uint8_t* const scales[1] = {w2s + (size_t)(col0 + n) * (F / 16) + g * 4};
-    f32x4_t acc[4][1];
-    dec_stream<1>(s_arow, ntok, F, codes, scales, lds, acc);
+    const uint8_t* const codes[1] = {w2 + (size_t)(cbase + n) * (F / 2)};
+    const uint8_t* const scales[1] = {w2s + (size_t)(cbase + n) * (F / 16)};
+    const size_t cstride = (size_t)(16 * kDecWaves) * (F / 2), sstride = (size_t)(16 * kDecWaves) * (F / 16);
     const float g2 = W.g2[tl.ex];
+    auto epi = [&](int j, const f32x4_t (&acc)[TGM][1]) {
+        const int col = cbase + j * (16 * kDecWaves) + n;
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-        float y = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float v = lane_group_sum(acc[tg][0][q]);
-            if (q == g) y = v;
+        for (int tg = 0; tg < TGM; ++tg) {
+            const float y = dec_result<TGM, 1>(acc, tg, 0, g);
+            const int r = tl.rb + tg * 4 + g;
+            if (r < tl.re) a.Y[(size_t)r * d + col] = y * g2;
         }
-        const int r = tl.rb + tg * 4 + g;
-        if (r < tl.re) a.Y[(size_t)r * d + col0 + n] = y * g2;
+    };
+    dec_stream<1, TGM, DEPTH, RGS, FULLA, SEG>(s_arow, ntok, F, codes, scales, cstride, sstride, lds, epi);
+}
+
+// Tile height of the decode path: 4 token rows (one group, deep weight prefetch)
+// when experts expect at most ~2 tokens, else 16 rows (four groups).
+int dec_rows(int T, int topk, int E) { return (long long)T * topk <= 2LL * E ? 4 : 16; }
+
+template <int MODE, int TGM, int DEPTH>
+static void launch_g1(const GemmArgs& a, dim3 grid, hipStream_t s) {
+    const int full = dec_lds_bytes(4 * TGM, a.d, true);
+    const dim3 blk(64 * kDecWaves);
+    if (full <= kFullALds) {
+        if (DEPTH % 4 == 0 && a.d % 1024 == 0)
+            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, (DEPTH % 4 == 0)>), grid, blk, full, s, a);
+        else
+            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false>), grid, blk, full, s, a);
+    } else {
+        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, 2, false, false>), grid, blk,
+                           dec_lds_bytes(4 * TGM, a.d, false), s, a);
     }
 }
 
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
-    dim3 grid(a.max_tiles, a.F / (16 * kDecWaves));
-    if (a.mode == 0) hipLaunchKernelGGL(dec_gemm1_kernel<0>, grid, dim3(64 * kDecWaves), 0, s, a);
-    else hipLaunchKernelGGL(dec_gemm1_kernel<1>, grid, dim3(64 * kDecWaves), 0, s, a);
+    dim3 grid(a.max_tiles, a.F / 32);
+    const bool small = dec_rows(a.T, a.topk, a.E) == 4;
+    if (small) {
+        if (a.mode == 0) launch_g1<0, 1, 4>(a, grid, s);
+        else launch_g1<1, 1, 4>(a, grid, s);
+    } else {
+        if (a.mode == 0) launch_g1<0, 4, 2>(a, grid, s);
+        else launch_g1<1, 4, 2>(a, grid, s);
+    }
     return hipGetLastError();
 }
 
+template <int TGM, int DEPTH>
+static void launch_g2(const GemmArgs& a, hipStream_t s) {
+    const int full = dec_lds_bytes(4 * TGM, a.F, true);
+    const dim3 blk(64 * kDecWaves);
+    constexpr bool kSeg = DEPTH % 4 == 0;
+    if (full <= kFullALds) {
+        const bool seg = kSeg && a.F % 1024 == 0;
+        if (a.d % (16 * kDecWaves * 4) == 0) {
+            const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 4));
+            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 4, true, kSeg>), grid, blk, full, s, a);
+            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 4, true, false>), grid, blk, full, s, a);
+        } else {
+            const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 2));
+            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg>), grid, blk, full, s, a);
+            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 2, true, false>), grid, blk, full, s, a);
+        }
+    } else {
+        hipLaunchKernelGGL((dec_gemm2_kernel<TGM, 2, 1, false, false>), dim3(a.max_tiles, a.d / (16 * kDecWaves)), blk,
+                           dec_lds_bytes(4 * TGM, a.F, false), s, a);
+    }
+}
+
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s) {
-    dim3 grid(a.max_tiles, a.d / (16 * kDecWaves));
-    hipLaunchKernelGGL(dec_gemm2_kernel, grid, dim3(64 * kDecWaves), 0, s, a);
+    if (dec_rows(a.T, a.topk, a.E) == 4) launch_g2<1, 4>(a, s);
+    else launch_g2<4, 2>(a, s);
     return hipGetLastError();
 }
 

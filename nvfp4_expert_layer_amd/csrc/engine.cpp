@@ -90,7 +90,7 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     const size_t d = p.d_model, F = p.d_ff;
     pl.KS = moe::router_ksplit((int)T, (int)E, (int)d);
     pl.path = resolve_path(p);
-    pl.BM = moe::gemm_bm(pl.path);
+    pl.BM = moe::gemm_bm(pl.path, (int)T, (int)k, (int)E);
     const size_t bm = pl.BM;
     pl.max_tiles = (int)((T * k + bm - 1) / bm + L + (p.has_shared ? (T + bm - 1) / bm : 0));
     pl.nblk = (int)((T + 255) / 256);
@@ -278,6 +278,7 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     moe::GemmArgs g{};
     g.T = p->num_tokens; g.d = p->d_model; g.F = p->d_ff; g.topk = p->top_k; g.L = p->num_local_experts;
     g.mode = p->mode;
+    g.E = p->num_experts;
     g.perm = at<int32_t>(workspace, pl.perm);
     g.tiles = at<int4>(workspace, pl.tiles);
     g.ntiles = at<int32_t>(workspace, pl.ntiles);

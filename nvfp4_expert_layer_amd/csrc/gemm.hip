@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-int gemm_bm(int path) { return path == 1 ? 16 : 64; }
+int gemm_bm(int path, int T, int topk, int E) { return path == 1 ? dec_rows(T, topk, E) : 64; }
 
 hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s) {
     dim3 grid(a.max_tiles, a.F / 64);

@@ -40,7 +40,7 @@ struct PermArgs {
 };
 
 struct GemmArgs {
-    int T, d, F, topk, L, mode;
+    int T, d, F, topk, L, mode, E;
     const int32_t* perm;          // [T*k]
     const int4* tiles;            // (group, row_begin, row_end, -)
     const int32_t* ntiles;
@@ -69,7 +69,8 @@ hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out,
 hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
-int gemm_bm(int path);            // rows per tile of the chosen path
+int gemm_bm(int path, int T, int topk, int E);   // rows per tile of the chosen path
+int dec_rows(int T, int topk, int E);
 hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s);

@@ -39,8 +39,9 @@ constexpr int kR1Pad = 8;       // bf16 elements of row padding in LDS
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, int T, int E, int d,
     int kslice, float* __restrict__ part, double* __restrict__ xn2, double* __restrict__ gn2) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kR1Tile][kR1BK + kR1Pad];
-    __shared__ __attribute__((aligned(16))) uint16_t gs[kR1Tile][kR1BK + kR1Pad];
+    // double-buffered LDS tiles: the next K chunk is loaded while this one runs on MFMA
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kR1Tile][kR1BK + kR1Pad];
+    __shared__ __attribute__((aligned(16))) uint16_t gs[2][kR1Tile][kR1BK + kR1Pad];
     const int t0 = blockIdx.x * kR1Tile, e0 = blockIdx.y * kR1Tile, ks = blockIdx.z;
     const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -51,47 +52,65 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // squared norms: thread tid < 64 -> token row t0+tid; 64..127 -> expert row e0+tid-64
-    double nrm = 0.0;
-    for (int k0 = kbeg; k0 < kend; k0 += kR1BK) {
-        // stage 64 rows x 64 bf16 of X and of G: 512 16-byte chunks each, 2 per thread
+    // 64 rows x 64 bf16 of X and of G per chunk: 512 16-byte pieces each, 2 per thread
+    u32x4_t vx[2], vg[2];
+    auto load = [&](int k0) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            int chunk = tid + c * 256;          // 0..511
-            int r = chunk >> 3, cc = (chunk & 7) * 8;
-            u32x4_t vx = {0u, 0u, 0u, 0u}, vg = {0u, 0u, 0u, 0u};
-            if (t0 + r < T) vx = *reinterpret_cast<const u32x4_t*>(X + (size_t)(t0 + r) * d + k0 + cc);
-            if (e0 + r < E) vg = *reinterpret_cast<const u32x4_t*>(G + (size_t)(e0 + r) * d + k0 + cc);
-            *reinterpret_cast<u32x4_t*>(&xs[r][cc]) = vx;
-            *reinterpret_cast<u32x4_t*>(&gs[r][cc]) = vg;
+            const int chunk = tid + c * 256;
+            const int r = chunk >> 3, cc = (chunk & 7) * 8;
+            vx[c] = u32x4_t{0u, 0u, 0u, 0u};
+            vg[c] = u32x4_t{0u, 0u, 0u, 0u};
+            if (t0 + r < T) vx[c] = *reinterpret_cast<const u32x4_t*>(X + (size_t)(t0 + r) * d + k0 + cc);
+            if (e0 + r < E) vg[c] = *reinterpret_cast<const u32x4_t*>(G + (size_t)(e0 + r) * d + k0 + cc);
         }
-        __syncthreads();
-        if (tid < 128) {
-            const uint16_t* row = tid < 64 ? xs[tid] : gs[tid - 64];
-            bool want = tid < 64 ? (blockIdx.y == 0) : (blockIdx.x == 0);
-            if (want) {
-                for (int j = 0; j < kR1BK; ++j) {
-                    double v = (double)bf16_bits_to_f32(row[j]);
-                    nrm = fma(v, v, nrm);
-                }
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int chunk = tid + c * 256;
+            const int r = chunk >> 3, cc = (chunk & 7) * 8;
+            *reinterpret_cast<u32x4_t*>(&xs[b][r][cc]) = vx[c];
+            *reinterpret_cast<u32x4_t*>(&gs[b][r][cc]) = vg[c];
+        }
+    };
+    // squared norms: thread tid < 64 -> token row t0+tid; 64..127 -> expert row e0+tid-64
+    double nrm = 0.0;
+    const bool want = tid < 64 ? (blockIdx.y == 0) : (tid < 128 && blockIdx.x == 0);
+    if (kbeg < kend) {
+        load(kbeg);
+        store(0);
+    }
+    __syncthreads();
+    int b = 0;
+    for (int k0 = kbeg; k0 < kend; k0 += kR1BK) {
+        const bool more = k0 + kR1BK < kend;
+        if (more) load(k0 + kR1BK);
+        if (want) {
+            const uint16_t* row = tid < 64 ? xs[b][tid] : gs[b][tid - 64];
+            for (int j = 0; j < kR1BK; ++j) {
+                const double v = (double)bf16_bits_to_f32(row[j]);
+                nrm = fma(v, v, nrm);
             }
         }
 #pragma unroll
         for (int kk = 0; kk < kR1BK; kk += 32) {
-            bf16x8_t a[2], b[2];
+            bf16x8_t a[2], bb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t*>(&xs[wm * 32 + i * 16 + (lane & 15)][kk + (lane >> 4) * 8]);
+                a[i] = *reinterpret_cast<const bf16x8_t*>(&xs[b][wm * 32 + i * 16 + (lane & 15)][kk + (lane >> 4) * 8]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                b[j] = *reinterpret_cast<const bf16x8_t*>(&gs[wn * 32 + j * 16 + (lane & 15)][kk + (lane >> 4) * 8]);
+                bb[j] = *reinterpret_cast<const bf16x8_t*>(&gs[b][wn * 32 + j * 16 + (lane & 15)][kk + (lane >> 4) * 8]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
+        if (more) store(b ^ 1);
         __syncthreads();
+        b ^= 1;
     }
     float* out = part + (size_t)ks * T * E;
 #pragma unroll
@@ -100,8 +119,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                int t = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
-                int e = e0 + wn * 32 + j * 16 + (lane & 15);
+                const int t = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+                const int e = e0 + wn * 32 + j * 16 + (lane & 15);
                 if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
             }
     if (tid < 64 && blockIdx.y == 0 && t0 + tid < T) xn2[(size_t)ks * T + t0 + tid] = nrm;
@@ -113,75 +132,29 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxKS = 16;          // split-K slices of the logits GEMM
+constexpr int kSlices = 16;         // K slices of one fp64 candidate dot product
+constexpr int kMaxCand = 64;        // candidates re-scored per pass
 constexpr int kSelWaves = 4;
 
-__device__ __forceinline__ double dot_f64(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g,
-                                          int d, int lane) {
-    // fp64 products of bf16 pairs are exact; a lane sums its elements in a fixed
-    // order, then the wave reduces in a fixed tree.  Loads are issued 8 chunks at
-    // a time so one latency covers d = 4096.
-    double s = 0.0;
-    for (int c0 = lane * 8; c0 < d; c0 += 512 * 8) {
-        u32x4_t vx[8], vg[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = c0 + j * 512;
-            const u32x4_t z = {0u, 0u, 0u, 0u};
-            vx[j] = c < d ? *reinterpret_cast<const u32x4_t*>(x + c) : z;
-            vg[j] = c < d ? *reinterpret_cast<const u32x4_t*>(g + c) : z;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t ax[4] = {vx[j].x, vx[j].y, vx[j].z, vx[j].w};
-            const uint32_t ag[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s = fma((double)__uint_as_float(ax[q] << 16), (double)__uint_as_float(ag[q] << 16), s);
-                s = fma((double)__uint_as_float(ax[q] & 0xFFFF0000u), (double)__uint_as_float(ag[q] & 0xFFFF0000u), s);
-            }
-        }
-    }
-    return wave_sum_f64(s);
-}
-
-// Wave-wide arg-max over `vals` (per-lane slots e = lane + 64 i), largest value,
-// ties -> lowest index; returns the index (or -1 if all are -inf / taken).
-template <int NS>
-__device__ __forceinline__ int wave_argmax(const double (&vals)[NS], int E, int lane) {
-    double best = -INFINITY;
-    int bidx = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        int e = lane + 64 * i;
-        if (e < E && (vals[i] > best || (vals[i] == best && e < bidx)) && vals[i] != -INFINITY) {
-            best = vals[i];
-            bidx = e;
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        double ob = __shfl_xor(best, o, 64);
-        int oi = __shfl_xor(bidx, o, 64);
-        if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
-    }
-    return bidx == 0x7FFFFFFF ? -1 : bidx;
-}
-
-template <int NS>
 __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
     int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ local_ids) {
-    // one workgroup per token: wave 0 bounds the logits and lists the candidates,
-    // all waves re-score candidates in fp64, wave 0 selects and normalises.
+    // one workgroup per token: bound every logit, list the candidates that can
+    // reach the top-k, re-score them in fp64, rank them, normalise the k weights.
     __shared__ int32_t s_cand[kMaxExperts];
     __shared__ double s_score[kMaxExperts];
+    __shared__ double s_part[kMaxCand * kSlices];
     __shared__ int32_t s_ncand;
+    __shared__ double s_lowk;
+    __shared__ int32_t s_sel_id[32];
+    __shared__ double s_sel_sc[32];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t = blockIdx.x;
     const uint16_t* xrow = X + (size_t)t * d;
     __shared__ double s_lo[kMaxExperts], s_hi[kMaxExperts];
+    __shared__ uint64_t s_key[kMaxExperts];
     {
         // bounds for every expert, spread over the whole workgroup; the split-K
         // partial sums are loaded together (KS <= kMaxKS) and added in slice order
@@ -209,78 +182,122 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
 #pragma unroll
             for (int s = 0; s < kMaxKS; ++s) { lh += pv[s]; gs2 += gv[s]; }
             const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
-            s_lo[e] = (double)lh - beta;
+            const double lo = (double)lh - beta;
+            s_lo[e] = lo;
             s_hi[e] = (double)lh + beta;
+            // rank key: lo rounded DOWN to fp32, made order-preserving as an
+            // unsigned integer, with the expert id below it (ties -> lower id first)
+            float lf = (float)lo;
+            uint32_t bits = __float_as_uint(lf);
+            if ((double)lf > lo)   // one fp32 step toward -inf (lo is finite)
+                bits = (lf > 0.0f) ? bits - 1u : (lf == 0.0f ? 0x80000001u : bits + 1u);
+            const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+            s_key[e] = ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
         }
     }
     __syncthreads();
-    if (wave == 0) {
-        double lo[NS], hi[NS];
+    // Candidate threshold: the k-th largest of the lower bounds rounded down to
+    // fp32 (keys in s_key).  It is <= the k-th largest exact lower bound, so the
+    // candidates it admits are a superset of the exact ones (all still re-scored
+    // in fp64).  An expert's rank is the number of keys above its own (keys are
+    // unique); the expert of rank k - 1 gives the threshold.
+    for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
+        const uint64_t key = s_key[e];
+        int rank = 0;
+        int f0 = 0;
+        for (; f0 + 16 <= E; f0 += 16) {
+            uint64_t w[16];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const int e = lane + 64 * i;
-            lo[i] = e < E ? s_lo[e] : -INFINITY;
-            hi[i] = e < E ? s_hi[e] : -INFINITY;
+            for (int q = 0; q < 16; ++q) w[q] = s_key[f0 + q];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) rank += (int)(w[q] > key);
         }
-        // lowk = k-th largest lower bound
-        double tmp[NS];
-#pragma unroll
-        for (int i = 0; i < NS; ++i) tmp[i] = lo[i];
-        int idx = -1;
-        for (int r = 0; r < topk; ++r) {
-            idx = wave_argmax<NS>(tmp, E, lane);
-#pragma unroll
-            for (int i = 0; i < NS; ++i)
-                if (lane + 64 * i == idx) tmp[i] = -INFINITY;
+        for (int f = f0; f < E; ++f) rank += (int)(s_key[f] > key);
+        if (rank == topk - 1) {
+            const uint32_t ord = (uint32_t)(key >> 32);
+            const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+            s_lowk = (double)__uint_as_float(bits);
         }
-        double v = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-            if (lane + 64 * i == idx) v = lo[i];
-        const double lowk = __shfl(v, idx & 63, 64);
-        // candidates (hi >= lowk), listed in increasing expert id
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-            const bool c = lane + 64 * i < E && hi[i] >= lowk;
-            const uint64_t m = __ballot(c);
-            if (c) s_cand[base + __popcll(m & ((1ull << lane) - 1ull))] = lane + 64 * i;
-            base += __popcll(m);
-        }
-        if (lane == 0) s_ncand = base;
+    }
+    if (threadIdx.x == 0) s_ncand = 0;
+    __syncthreads();
+    // candidates: every expert whose upper bound reaches lowk (the order of the
+    // list does not matter: the final ranking is by (score, id))
+    {
+        const double lowk = s_lowk;
+        for (int e = threadIdx.x; e < E; e += 64 * kSelWaves)
+            if (s_hi[e] >= lowk) s_cand[atomicAdd(&s_ncand, 1)] = e;
     }
     __syncthreads();
     const int nc = s_ncand;
-    for (int c = wave; c < nc; c += kSelWaves) {
-        const int e = s_cand[c];
-        const double sc = dot_f64(xrow, G + (size_t)e * d, d, lane);
-        if (lane == 0) s_score[c] = sc;
+    // fp64 re-scoring of the candidates, kMaxCand at a time: item (c, s) =
+    // candidate c over K slice s of kSlices; the slice sums of a candidate are
+    // added in slice order by one thread, so the score is deterministic.
+    for (int cb = 0; cb < nc; cb += kMaxCand) {
+        const int ncb = min(kMaxCand, nc - cb);
+        for (int i0 = 0; i0 < ncb * kSlices; i0 += 64 * kSelWaves) {
+            const int i = i0 + threadIdx.x;
+            if (i < ncb * kSlices) {
+                const int c = i / kSlices, sl = i - c * kSlices;
+                const int len = d / kSlices, k0 = sl * len;
+                const uint16_t* gx = xrow + k0;
+                const uint16_t* gg = G + (size_t)s_cand[cb + c] * d + k0;
+                double acc4[4] = {0.0, 0.0, 0.0, 0.0};   // four chains, added in a fixed order
+                for (int kk = 0; kk < len; kk += 64) {
+                    u32x4_t vx[8], vg[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const bool in = kk + j * 8 < len;
+                        vx[j] = in ? *reinterpret_cast<const u32x4_t*>(gx + kk + j * 8) : u32x4_t{0u, 0u, 0u, 0u};
+                        vg[j] = in ? *reinterpret_cast<const u32x4_t*>(gg + kk + j * 8) : u32x4_t{0u, 0u, 0u, 0u};
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t ax[4] = {vx[j].x, vx[j].y, vx[j].z, vx[j].w};
+                        const uint32_t ag[4] = {vg[j].x, vg[j].y, vg[j].z, vg[j].w};
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc4[q] = fma((double)__uint_as_float(ax[q] << 16), (double)__uint_as_float(ag[q] << 16),
+                                          acc4[q]);
+                            acc4[q] = fma((double)__uint_as_float(ax[q] & 0xFFFF0000u),
+                                          (double)__uint_as_float(ag[q] & 0xFFFF0000u), acc4[q]);
+                        }
+                    }
+                }
+                s_part[i] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+            }
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < ncb; c += 64 * kSelWaves) {
+            double sc = 0.0;
+            for (int sl = 0; sl < kSlices; ++sl) sc += s_part[c * kSlices + sl];
+            s_score[cb + c] = sc;
+        }
+        __syncthreads();
+    }
+    // top-k among candidates by (fp64 score desc, id asc): a candidate's rank is
+    // the number of candidates ahead of it; ranks 0..k-1 are the selected slots
+    for (int c = threadIdx.x; c < nc; c += 64 * kSelWaves) {
+        const double v = s_score[c];
+        const int id = s_cand[c];
+        int rank = 0;
+        for (int f = 0; f < nc; ++f) {
+            const double w = s_score[f];
+            rank += (int)(w > v) | ((int)(w == v) & (int)(s_cand[f] < id));
+        }
+        if (rank < topk) {
+            s_sel_id[rank] = id;
+            s_sel_sc[rank] = v;
+        }
     }
     __syncthreads();
     if (wave != 0) return;
-    // top-k among candidates by (fp64 score desc, id asc): candidate slots c = lane + 64 i
-    double sc[NS];
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        const int c = lane + 64 * i;
-        sc[i] = c < nc ? s_score[c] : -INFINITY;
-    }
-    int my_id = -1;
-    double my_score = 0.0, top_score = 0.0;
-    for (int r = 0; r < topk; ++r) {
-        const int idx = wave_argmax<NS>(sc, nc, lane);
-        double v = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-            if (lane + 64 * i == idx) { v = sc[i]; sc[i] = -INFINITY; }
-        v = __shfl(v, idx & 63, 64);    // broadcast from the owner lane
-        if (r == 0) top_score = v;
-        if (lane == r) { my_id = s_cand[idx]; my_score = v; }
-    }
-    // softmax over the k selected fp64 scores
-    const double z = lane < topk ? exp(my_score - top_score) : 0.0;
+    // softmax over the k selected fp64 scores (slot 0 holds the largest)
+    const double my_score = lane < topk ? s_sel_sc[lane] : 0.0;
+    const double z = lane < topk ? exp(my_score - s_sel_sc[0]) : 0.0;
     const double zs = wave_sum_f64(z);
     if (lane < topk) {
+        const int my_id = s_sel_id[lane];
         const size_t o = (size_t)t * topk + lane;
         topk_ids[o] = my_id;
         topk_w[o] = (float)(z / zs);
@@ -474,19 +491,8 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
                        a.part, a.xn2, a.gn2);
     dim3 g2(a.T);
-    const int ns = (a.E + 63) / 64;
-#define SEL(NSV)                                                                                       \
-    hipLaunchKernelGGL(router_select_kernel<NSV>, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, \
-                       a.xn2, a.gn2, a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w,   \
-                       a.local_ids)
-    if (ns <= 1) SEL(1);
-    else if (ns <= 2) SEL(2);
-    else if (ns <= 4) SEL(4);
-    else if (ns <= 6) SEL(6);
-    else if (ns <= 8) SEL(8);
-    else if (ns <= 12) SEL(12);
-    else SEL(16);
-#undef SEL
+    hipLaunchKernelGGL(router_select_kernel, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, a.xn2, a.gn2,
+                       a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
     return hipGetLastError();
 }
 
