@@ -11,8 +11,9 @@
  *     num_local_experts) of the routed experts; globally routed expert ids are
  *     mapped to shard-relative indices and token-expert pairs outside the shard
  *     are dropped; the output is this shard's partial sum, which the caller adds
- *     up across shards with an ordinary all-reduce; the per-expert scale tensors
- *     of a shard may start at any expert (no alignment beyond 4 bytes); one
+ *     up across shards with an ordinary all-reduce; the weight tensors of a
+ *     shard may start at any expert (every expert's codes and scales span a
+ *     multiple of 16 bytes, so a slice of an aligned tensor stays aligned); one
  *     scratch pool serves every layer;
  *   - section "b12x 버전이 실제 NVFP4 체크포인트를 읽어들이도록 만들기": expert
  *     weights are packed FP4 codes, FP8 (E4M3) block scales clamped to 448 and a
@@ -46,7 +47,9 @@
  *
  * Conventions of every entry point:
  *   - All tensor pointers are DEVICE pointers (HIP), caller-owned, row-major,
- *     dense, 4-byte aligned at least (bf16 tensors 16-byte aligned).
+ *     dense; bf16 tensors, FP4 codes and E4M3 scales 16-byte aligned, fp32 and
+ *     int32 tensors 4-byte aligned (MOE_NVFP4_ERR_INVALID_ARG otherwise for the
+ *     weights).
  *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream); no
  *     host synchronisation, no allocation, no hidden global state.  Inputs are
  *     never modified.

@@ -143,6 +143,11 @@ int check_weights(const moe_nvfp4_weights* w, const char* what) {
     if (!w) return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s weights are NULL", what);
     if (!w->w13 || !w->w13_scale || !w->w13_global || !w->w2 || !w->w2_scale || !w->w2_global)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s weights have a NULL tensor pointer", what);
+    auto mis = [](const void* q, uintptr_t al) { return (reinterpret_cast<uintptr_t>(q) & (al - 1)) != 0; };
+    if (mis(w->w13, 16) || mis(w->w13_scale, 16) || mis(w->w2, 16) || mis(w->w2_scale, 16))
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s weight codes and scales must be 16-byte aligned", what);
+    if (mis(w->w13_global, 4) || mis(w->w2_global, 4))
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "%s global scales must be 4-byte aligned", what);
     return MOE_NVFP4_OK;
 }
 
@@ -245,6 +250,9 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     int st = moe_nvfp4_validate(p, workspace_bytes, nullptr);
     if (st) return st;
     if (!hidden || !gate_w || !out) return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w/out is NULL");
+    if (((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(gate_w) |
+          reinterpret_cast<uintptr_t>(out)) & 15u) != 0)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w/out must be 16-byte aligned");
     if ((st = check_weights(local, "local"))) return st;
     if (p->has_shared) {
         if ((st = check_weights(shared, "shared"))) return st;
@@ -313,6 +321,8 @@ int moe_nvfp4_route(const moe_nvfp4_problem* p, const void* hidden, const void* 
     int st = moe_nvfp4_validate(p, workspace_bytes, nullptr);
     if (st) return st;
     if (!hidden || !gate_w) return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w is NULL");
+    if (((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(gate_w)) & 15u) != 0)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "hidden/gate_w must be 16-byte aligned");
     Plan pl;
     make_plan(*p, pl);
     if (!workspace && pl.total) return fail(MOE_NVFP4_ERR_INVALID_ARG, "workspace is NULL");

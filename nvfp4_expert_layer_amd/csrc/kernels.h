@@ -70,6 +70,7 @@ hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 int gemm_bm(int path, int T, int topk, int E);   // rows per tile of the chosen path
+int pf_rows();                                    // rows per tile of the prefill GEMMs
 int dec_rows(int T, int topk, int E);
 hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);

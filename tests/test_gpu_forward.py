@@ -25,9 +25,7 @@ _layers = {}
 def layer(name, **kw):
     key = (name, tuple(sorted(kw.items())))
     if key not in _layers:
-        w = workloads.WORKLOADS[name] if name in workloads.WORKLOADS else None
-        if w is None:
-            w = MID
+        w = workloads.WORKLOADS[name] if name in workloads.WORKLOADS else LOCAL[name]
         if kw:
             w = workloads.replace(w, **kw)
         _layers[key] = Layer(w)
@@ -37,6 +35,12 @@ def layer(name, **kw):
 # A mid-size layer: several M and N tiles, ragged token count, E not a power of 2.
 MID = workloads.Workload("mid", T=200, d=512, F=256, E=24, k=4, offset=0, L=24, has_shared=True,
                          mode=W4A16, hidden_seed=7, gate_seed=7, weight_seed=7, gate_std=0.05)
+# Odd widths and heavy experts: d % 256 == 128 (a half-filled column block in the
+# down projection's 256-wide tiles), ~240 pairs per expert plus 600 shared rows
+# (experts spanning several 256-row tiles, ragged last tiles).
+WIDE = workloads.Workload("wide", T=600, d=384, F=384, E=5, k=2, offset=0, L=5, has_shared=True,
+                          mode=W4A16, hidden_seed=9, gate_seed=9, weight_seed=9, gate_std=0.05)
+LOCAL = {"mid": MID, "wide": WIDE}
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
@@ -60,6 +64,20 @@ def test_mid_layer_full_output(mode, path, offset, L, shared):
     require_gpu()
     lay = layer("mid")
     log(f"mid full output mode={mode} path={path} offset={offset} L={L} shared={shared}")
+    out = lay.run(offset, L, shared, mode, path)
+    ref = lay.oracle_full(offset, L, shared, mode)
+    err = rel_err(out, ref["out"])
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(mode)
+
+
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("offset,L,shared", [(0, 5, True), (1, 3, False)])
+def test_wide_layer_full_output(mode, path, offset, L, shared):
+    require_gpu()
+    lay = layer("wide")
+    log(f"wide full output mode={mode} path={path} offset={offset} L={L} shared={shared}")
     out = lay.run(offset, L, shared, mode, path)
     ref = lay.oracle_full(offset, L, shared, mode)
     err = rel_err(out, ref["out"])
