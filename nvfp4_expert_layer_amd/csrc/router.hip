@@ -135,6 +135,7 @@ constexpr int kMaxKS = 16;          // split-K slices of the logits GEMM
 constexpr int kSlices = 16;         // K slices of one fp64 candidate dot product
 constexpr int kMaxCand = 64;        // candidates re-scored per pass
 constexpr int kSelWaves = 4;
+constexpr int kWideSelectTokens = 1024;   // from here on, one wave per token
 
 __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
@@ -298,6 +299,178 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
     const double zs = wave_sum_f64(z);
     if (lane < topk) {
         const int my_id = s_sel_id[lane];
+        const size_t o = (size_t)t * topk + lane;
+        topk_ids[o] = my_id;
+        topk_w[o] = (float)(z / zs);
+        const int lam = my_id - offset;
+        local_ids[o] = (lam >= 0 && lam < L) ? lam : -1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// R2 for many tokens: the same certified selection, one wave per token (four
+// tokens per workgroup, waves independent).  Experts e = lane + 64 s, s < EPL
+// (the smallest instantiated EPL with 64 EPL >= E).
+//   bounds  -> registers;
+//   threshold: the k-th largest rank key by a tournament (k rounds of a wave
+//     max; keys are unique, so exactly one lane owns each maximum);
+//   candidates (hi >= threshold), in ascending id order -> per-wave LDS list;
+//   fp64 re-scoring: K in chunks of 512 (8 elements per lane, converted to fp64
+//     once per chunk and shared by up to 16 candidates whose loads are all in
+//     flight together); per-lane partial sums are reduced in a fixed butterfly
+//     order, so scores are deterministic;
+//   rank of each candidate by (score desc, id asc), softmax over the first k.
+// ---------------------------------------------------------------------------
+constexpr int kWTok = 4;            // tokens (waves) per workgroup
+constexpr int kWGroup = 8;          // candidates scored together
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+        const uint64_t w = ((uint64_t)hi << 32) | lo;
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+template <int kWSlots>
+__global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
+    const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
+    int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ local_ids) {
+    __shared__ int32_t s_cid[kWTok][kMaxExperts];
+    __shared__ double s_csc[kWTok][kMaxExperts];
+    __shared__ int32_t s_sel_id[kWTok][32];
+    __shared__ double s_sel_sc[kWTok][32];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int t = blockIdx.x * kWTok + w;
+    if (t >= T) return;                                  // whole wave; no workgroup barriers below
+    int32_t* cid = s_cid[w];
+    double* csc = s_csc[w];
+
+    // ---- bounds (same arithmetic and order as router_select_kernel) ----
+    const double u = 1.0 / 8388608.0;
+    const double n = (double)(d + KS);
+    const double gamma = n * u / (1.0 - n * u) * (1.0 + 1e-6);
+    const double tiny = (double)d * 1.1754943508222875e-38;
+    double xs2 = 0.0;
+    for (int s = 0; s < KS; ++s) xs2 += xn2[(size_t)s * T + t];
+    const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
+    double hi[kWSlots];
+    uint64_t key[kWSlots];
+#pragma unroll
+    for (int sl = 0; sl < kWSlots; ++sl) {
+        hi[sl] = -INFINITY;
+        key[sl] = 0;                                     // below every valid key
+        const int e = lane + 64 * sl;
+        if (e < E) {
+            float lh = 0.f;
+            double gs2 = 0.0;
+            for (int s = 0; s < KS; ++s) {
+                lh += part[((size_t)s * T + t) * E + e];
+                gs2 += gn2[(size_t)s * E + e];
+            }
+            const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
+            const double lo = (double)lh - beta;
+            hi[sl] = (double)lh + beta;
+            float lf = (float)lo;
+            uint32_t bits = __float_as_uint(lf);
+            if ((double)lf > lo) bits = (lf > 0.0f) ? bits - 1u : (lf == 0.0f ? 0x80000001u : bits + 1u);
+            const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+            key[sl] = ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+        }
+    }
+
+    // ---- threshold: k rounds of a wave max over the remaining keys ----
+    uint64_t kth = 0;
+    for (int r = 0; r < topk; ++r) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int sl = 0; sl < kWSlots; ++sl) m = key[sl] > m ? key[sl] : m;
+        kth = wave_max_u64(m);
+#pragma unroll
+        for (int sl = 0; sl < kWSlots; ++sl) key[sl] = key[sl] == kth ? 0 : key[sl];
+    }
+    const uint32_t kord = (uint32_t)(kth >> 32);
+    const double lowk = (double)__uint_as_float((kord & 0x80000000u) ? (kord & 0x7FFFFFFFu) : ~kord);
+
+    // ---- candidates in ascending id order ----
+    int nc = 0;
+#pragma unroll
+    for (int sl = 0; sl < kWSlots; ++sl) {
+        const bool c = hi[sl] >= lowk;
+        const uint64_t mask = __ballot(c);
+        if (c) cid[nc + __popcll(mask & ((1ull << lane) - 1ull))] = lane + 64 * sl;
+        nc += __popcll(mask);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- fp64 re-scoring ----
+    const uint16_t* xrow = X + (size_t)t * d;
+    for (int g0 = 0; g0 < nc; g0 += kWGroup) {
+        const int ng = min(kWGroup, nc - g0);
+        int ids[kWGroup];
+#pragma unroll
+        for (int c = 0; c < kWGroup; ++c) ids[c] = cid[g0 + (c < ng ? c : 0)];
+        double acc[kWGroup];
+#pragma unroll
+        for (int c = 0; c < kWGroup; ++c) acc[c] = 0.0;
+        for (int k0 = lane * 8; k0 < d; k0 += 512) {
+            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xrow + k0);
+            double xd[8];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xd[2 * q] = (double)__uint_as_float(xw[q] << 16);
+                xd[2 * q + 1] = (double)__uint_as_float(xw[q] & 0xFFFF0000u);
+            }
+            u32x4_t gv[kWGroup];
+#pragma unroll
+            for (int c = 0; c < kWGroup; ++c)
+                gv[c] = *reinterpret_cast<const u32x4_t*>(G + (size_t)ids[c] * d + k0);
+#pragma unroll
+            for (int c = 0; c < kWGroup; ++c) {
+                const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[c] = fma(xd[2 * q], (double)__uint_as_float(gw[q] << 16), acc[c]);
+                    acc[c] = fma(xd[2 * q + 1], (double)__uint_as_float(gw[q] & 0xFFFF0000u), acc[c]);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kWGroup; ++c) {
+            const double sc = wave_sum_f64(acc[c]);
+            if (c < ng && lane == 0) csc[g0 + c] = sc;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- rank by (score desc, id asc); ranks 0..k-1 are the slots ----
+    for (int c = lane; c < nc; c += 64) {
+        const double v = csc[c];
+        const int id = cid[c];
+        int rank = 0;
+        for (int f = 0; f < nc; ++f) {
+            const double x = csc[f];
+            rank += (int)(x > v) | ((int)(x == v) & (int)(cid[f] < id));
+        }
+        if (rank < topk) {
+            s_sel_id[w][rank] = id;
+            s_sel_sc[w][rank] = v;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const double my_score = lane < topk ? s_sel_sc[w][lane] : 0.0;
+    const double z = lane < topk ? exp(my_score - s_sel_sc[w][0]) : 0.0;
+    const double zs = wave_sum_f64(z);
+    if (lane < topk) {
+        const int my_id = s_sel_id[w][lane];
         const size_t o = (size_t)t * topk + lane;
         topk_ids[o] = my_id;
         topk_w[o] = (float)(z / zs);
@@ -490,9 +663,21 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     dim3 g1((a.T + kR1Tile - 1) / kR1Tile, (a.E + kR1Tile - 1) / kR1Tile, KS);
     hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
                        a.part, a.xn2, a.gn2);
-    dim3 g2(a.T);
-    hipLaunchKernelGGL(router_select_kernel, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, a.xn2, a.gn2,
-                       a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+    if (a.T >= kWideSelectTokens) {
+        // many tokens: one wave per token (throughput)
+        dim3 g2((a.T + kWTok - 1) / kWTok);
+        auto k = a.E <= 128 ? router_select_wave_kernel<2>
+                 : a.E <= 320 ? router_select_wave_kernel<5>
+                 : a.E <= 512 ? router_select_wave_kernel<8>
+                              : router_select_wave_kernel<kMaxExperts / 64>;
+        hipLaunchKernelGGL(k, g2, dim3(64 * kWTok), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
+                           a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+    } else {
+        // few tokens: a workgroup per token (latency)
+        dim3 g2(a.T);
+        hipLaunchKernelGGL(router_select_kernel, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, a.xn2,
+                           a.gn2, a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+    }
     return hipGetLastError();
 }
 

@@ -76,6 +76,23 @@ def test_route_zero_tokens_tie_to_lowest_ids():
     _check(x, G, w, 0, w.E)
 
 
+def test_route_wide_select_zero_tokens_and_shard():
+    """T >= 1024 takes the one-wave-per-token selection: zero tokens (every expert
+    a candidate) and a shard filter, against the oracle."""
+    require_gpu()
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=1100)
+    x = workloads.gen_hidden(w, "cuda")
+    for t in (0, 63, 64, 1099):
+        x[t] = 0
+    G = workloads.gen_gate(w, "cuda")
+    ids, wts, *_ = _route_gpu(x, G.t().contiguous(), w, 0, w.E, True)
+    for t in (0, 63, 64, 1099):
+        assert ids[t].tolist() == list(range(w.k))
+        assert np.allclose(wts[t], 1.0 / w.k, rtol=0, atol=1e-7)
+    amb, diff, P = _check(x, G, w, 100, 150)
+    log(f"  wide select: ambiguous {amb}, differing {diff}, P={P}")
+
+
 def test_route_tiny_problem_odd_shapes():
     """T not a multiple of any tile, E not a multiple of 64, k = 1 and k = E."""
     require_gpu()
