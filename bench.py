@@ -19,6 +19,7 @@ headline workload (the T=64 expert-shard decode step), with:
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +40,56 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HEADLINE = "decode_shard0_w4a16"
 SECONDARY = "prefill_all_w4a4"
 STAGES = ["route_permute", "act_quant", "gemm1_swiglu", "gemm2", "combine"]
+CSRC = os.path.join(ROOT, "nvfp4_expert_layer_amd", "csrc")
+# sources whose machine code the dominant kernel of each path is built from
+KERNEL_SOURCES = {"decode": ["decode.hip", "device_common.h", "kernels.h"],
+                  "prefill": ["prefill.hip", "device_common.h", "kernels.h"]}
+
+
+def kernel_source_hash(path):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[path]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary profiles/traffic_gemm1_<workload>.txt (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy's reading), or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    fn = os.path.join(ROOT, "profiles", f"traffic_gemm1_{workload}.txt")
+    if not os.path.exists(fn):
+        return None
+    vals = {}
+    with open(fn) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash(path):
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain copy of known size in one elementwise kernel (y = x + 0, so that
+    it is a kernel dispatch and not a DMA blit), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters: each dispatch reads and writes nbytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.add(src, 0, out=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps, "ms": round(dt * 1e3, 3),
+                      "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1)}), flush=True)
 
 
 class HipEvents:
@@ -153,12 +204,12 @@ def bench_workload(name, steps, warmup, hip):
     if decode:
         ach = alg["g1_bytes"] / g1_s / 1e9
         roof = {"kernel": "gemm1_swiglu", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode", name),
                 "algorithmic_bytes_per_launch": int(alg["g1_bytes"]), "launch_us": round(g1_ms * 1e3, 2)}
     else:
         ach = alg["g1_flops"] / g1_s / 1e12
         roof = {"kernel": "gemm1_swiglu", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill", name),
                 "algorithmic_flops_per_launch": alg["g1_flops"], "launch_us": round(g1_ms * 1e3, 2)}
     layer_hbm_frac = alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3)
     layer_mfma_frac = alg["layer_flops"] / (BF16_PEAK_TFLOPS * 1e12) / (ms * 1e-3)
@@ -231,7 +282,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=8)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel source hashes and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(json.dumps({p: kernel_source_hash(p) for p in KERNEL_SOURCES}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this layer runs on one GPU: the expert shard is exercised by running one "
                                    "shard's experts locally; --gpus must be 1"}))
@@ -243,6 +300,9 @@ def main():
         cpu = cpu_baseline(args.workload if not args.all else HEADLINE, args.cpu_sample)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     nv.lib()
     hip = HipEvents()
     for name in names:
