@@ -306,17 +306,20 @@ __device__ __forceinline__ DecTile dec_tile(const GemmArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMM1 + SwiGLU: a workgroup = 32 SwiGLU columns of a tile of <= 4 TGM token
-// rows; waves 0,1 stream the gate rows of columns [c0, c0+16) and [c0+16, c0+32),
-// waves 2,3 the matching up rows; the up results meet the gate results in LDS.
-// grid (max_tiles, F / 32).
+// GEMM1 + SwiGLU: a workgroup = 32 RG SwiGLU columns of a tile of <= 4 TGM
+// token rows; in row group j < RG, waves 0,1 stream the gate rows of columns
+// [c0 + 32 j, +16) and [c0 + 32 j + 16, +16), waves 2,3 the matching up rows (the
+// prefetch ring runs on across row groups); the up results meet the gate
+// results in LDS.  grid (max_tiles, F / (32 RG)).
 // ---------------------------------------------------------------------------
-template <int MODE, int TGM, int DEPTH, bool FULLA, bool SEG>
+template <int MODE, int TGM, int DEPTH, bool FULLA, bool SEG, int RG>
 __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
     constexpr int ROWS = 4 * TGM;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     __shared__ const uint16_t* s_arow[ROWS];
-    __shared__ float s_up[2][TGM][64];
+    // up results of row group j at [j & 1]: a gate wave reads group j before it
+    // reaches the barrier of group j + 1, so group j + 2 can reuse the buffer
+    __shared__ float s_up[2][2][TGM][64];
     if ((int)blockIdx.x >= *a.ntiles) return;
     const DecTile tl = dec_tile(a);
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = wave & 1;                       // which 16 columns
     const bool is_up = wave >= 2;
-    const int col0 = blockIdx.y * 32 + half * 16;
+    const int col0 = blockIdx.y * (32 * RG) + half * 16;
     const int n = lane & 15, g = lane >> 4;
     const int ntok = tl.re - tl.rb;
     const uint16_t* act_in = MODE == 0 ? a.hidden : a.hq;
@@ -341,20 +344,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
     const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2)};
     const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16)};
     const float g13 = W.g13[tl.ex];
-    const int col = col0 + n;
-    auto epi = [&](int, const f32x4_t (&acc)[TGM][1]) {
+    auto epi = [&](int j, const f32x4_t (&acc)[TGM][1]) {
+        const int col = col0 + 32 * j + n;
         float v[TGM];
 #pragma unroll
         for (int tg = 0; tg < TGM; ++tg) v[tg] = dec_result<TGM, 1>(acc, tg, 0, g) * g13;
         if (is_up) {
 #pragma unroll
-            for (int tg = 0; tg < TGM; ++tg) s_up[half][tg][lane] = v[tg];
+            for (int tg = 0; tg < TGM; ++tg) s_up[j & 1][half][tg][lane] = v[tg];
         }
         __syncthreads();
         if (!is_up) {
 #pragma unroll
             for (int tg = 0; tg < TGM; ++tg) {
-                const float gt = v[tg], up = s_up[half][tg][lane];
+                const float gt = v[tg], up = s_up[j & 1][half][tg][lane];
                 float av = gt / (1.0f + expf(-gt)) * up;
                 if (MODE == 1) {
                     // NVFP4 quantize-dequantize over the 16 columns of this lane group
@@ -370,7 +373,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
             }
         }
     };
-    dec_stream<1, TGM, DEPTH, 1, FULLA, SEG>(s_arow, ntok, d, codes, scales, 0, 0, lds, epi);
+    const size_t cstride = (size_t)32 * (d / 2), sstride = (size_t)32 * (d / 16);
+    dec_stream<1, TGM, DEPTH, RG, FULLA, SEG>(s_arow, ntok, d, codes, scales, cstride, sstride, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,45 +418,55 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
 // when experts expect at most ~2 tokens, else 16 rows (four groups).
 int dec_rows(int T, int topk, int E) { return (long long)T * topk <= 2LL * E ? 4 : 16; }
 
+constexpr int kG1RowGroups = 4;     // row groups per GEMM1 wave (F % (32 RG) == 0 required)
+constexpr int kG1Depth = 4;         // prefetch ring depth of the small-tile GEMM1
+
 template <int MODE, int TGM, int DEPTH>
-static void launch_g1(const GemmArgs& a, dim3 grid, hipStream_t s) {
+static void launch_g1(const GemmArgs& a, hipStream_t s) {
     const int full = dec_lds_bytes(4 * TGM, a.d, true);
     const dim3 blk(64 * kDecWaves);
-    if (full <= kFullALds) {
+    constexpr int RG = kG1RowGroups;
+    if (full <= kFullALds && a.F % (32 * RG) == 0) {
+        const dim3 grid(a.max_tiles, a.F / (32 * RG));
         if (DEPTH % 4 == 0 && a.d % 1024 == 0)
-            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, (DEPTH % 4 == 0)>), grid, blk, full, s, a);
+            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, (DEPTH % 4 == 0), RG>), grid, blk, full, s, a);
         else
-            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false>), grid, blk, full, s, a);
+            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, RG>), grid, blk, full, s, a);
+    } else if (full <= kFullALds) {
+        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, 1>), dim3(a.max_tiles, a.F / 32), blk,
+                           full, s, a);
     } else {
-        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, 2, false, false>), grid, blk,
+        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, 2, false, false, 1>), dim3(a.max_tiles, a.F / 32), blk,
                            dec_lds_bytes(4 * TGM, a.d, false), s, a);
     }
 }
 
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
-    dim3 grid(a.max_tiles, a.F / 32);
     const bool small = dec_rows(a.T, a.topk, a.E) == 4;
     if (small) {
-        if (a.mode == 0) launch_g1<0, 1, 4>(a, grid, s);
-        else launch_g1<1, 1, 4>(a, grid, s);
+        if (a.mode == 0) launch_g1<0, 1, kG1Depth>(a, s);
+        else launch_g1<1, 1, kG1Depth>(a, s);
     } else {
-        if (a.mode == 0) launch_g1<0, 4, 2>(a, grid, s);
-        else launch_g1<1, 4, 2>(a, grid, s);
+        if (a.mode == 0) launch_g1<0, 4, 2>(a, s);
+        else launch_g1<1, 4, 2>(a, s);
     }
     return hipGetLastError();
 }
+
+constexpr int kG2RowGroups = 4;     // row groups per GEMM2 wave
 
 template <int TGM, int DEPTH>
 static void launch_g2(const GemmArgs& a, hipStream_t s) {
     const int full = dec_lds_bytes(4 * TGM, a.F, true);
     const dim3 blk(64 * kDecWaves);
     constexpr bool kSeg = DEPTH % 4 == 0;
+    constexpr int RG = kG2RowGroups;
     if (full <= kFullALds) {
         const bool seg = kSeg && a.F % 1024 == 0;
-        if (a.d % (16 * kDecWaves * 4) == 0) {
-            const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 4));
-            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 4, true, kSeg>), grid, blk, full, s, a);
-            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 4, true, false>), grid, blk, full, s, a);
+        if (a.d % (16 * kDecWaves * RG) == 0) {
+            const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * RG));
+            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, RG, true, kSeg>), grid, blk, full, s, a);
+            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, RG, true, false>), grid, blk, full, s, a);
         } else {
             const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 2));
             if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg>), grid, blk, full, s, a);
