@@ -128,119 +128,141 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// R2: certified top-k per token (one wave per token).
+// R2 for few tokens (latency): one workgroup of 1024 threads per token.
+//   bounds: thread e < E takes expert e (all of its split-K partial loads in one
+//     batch);
+//   threshold: wave 0 runs a tournament (k rounds of a wave max) over the
+//     unique rank keys;
+//   candidates: hi >= threshold, listed in any order (the final rank is by
+//     (score, id));
+//   fp64 re-scoring: item (candidate c, K slice s) for kSlices slices of K, so
+//     each item's loads go out together; the slice sums of a candidate are
+//     added in slice order by one thread (deterministic);
+//   rank by (score desc, id asc), softmax over the first k.
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxKS = 16;          // split-K slices of the logits GEMM
-constexpr int kSlices = 16;         // K slices of one fp64 candidate dot product
-constexpr int kMaxCand = 64;        // candidates re-scored per pass
-constexpr int kSelWaves = 4;
+constexpr int kSlices = 64;         // at most this many K slices of one fp64 candidate dot product
+constexpr int kSelThreads = 1024;
 constexpr int kWideSelectTokens = 1024;   // from here on, one wave per token
 
-__global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+        const uint64_t w = ((uint64_t)hi << 32) | lo;
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// Rank key of a lower bound: lo rounded DOWN to fp32, made order-preserving as
+// an unsigned integer, with the expert id below it (equal values: lower id
+// first).  Keys are unique; 0 is below every key.
+__device__ __forceinline__ uint64_t rank_key(double lo, int e) {
+    float lf = (float)lo;
+    uint32_t bits = __float_as_uint(lf);
+    if ((double)lf > lo)   // one fp32 step toward -inf (lo is finite)
+        bits = (lf > 0.0f) ? bits - 1u : (lf == 0.0f ? 0x80000001u : bits + 1u);
+    const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
+// The fp32 lower bound a rank key was made from.
+__device__ __forceinline__ double key_value(uint64_t key) {
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return (double)__uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+__global__ __launch_bounds__(kSelThreads) void router_select_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
     int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ local_ids) {
-    // one workgroup per token: bound every logit, list the candidates that can
-    // reach the top-k, re-score them in fp64, rank them, normalise the k weights.
     __shared__ int32_t s_cand[kMaxExperts];
     __shared__ double s_score[kMaxExperts];
-    __shared__ double s_part[kMaxCand * kSlices];
+    __shared__ double s_part[kSelThreads];
+    __shared__ double s_hi[kMaxExperts];
+    __shared__ uint64_t s_key[kMaxExperts];
     __shared__ int32_t s_ncand;
     __shared__ double s_lowk;
     __shared__ int32_t s_sel_id[32];
     __shared__ double s_sel_sc[32];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = blockIdx.x;
     const uint16_t* xrow = X + (size_t)t * d;
-    __shared__ double s_lo[kMaxExperts], s_hi[kMaxExperts];
-    __shared__ uint64_t s_key[kMaxExperts];
+    if (tid == 0) s_ncand = 0;
     {
-        // bounds for every expert, spread over the whole workgroup; the split-K
-        // partial sums are loaded together (KS <= kMaxKS) and added in slice order
-        const double u = 1.0 / 8388608.0;                  // bound factor gamma_n, n = d + KS, u' = 2^-23
+        // Bounds: the split-K partial sums are added in slice order.  The fp32
+        // logit differs from the exact dot product by at most
+        // gamma_n ||x|| ||g_e|| + d 2^-126 with n = d + KS (see the file header).
+        const double u = 1.0 / 8388608.0;
         const double n = (double)(d + KS);
         const double gamma = n * u / (1.0 - n * u) * (1.0 + 1e-6);
-        const double tiny = (double)d * 1.1754943508222875e-38;   // d * 2^-126
-        double xv[kMaxKS];
+        const double tiny = (double)d * 1.1754943508222875e-38;
+        const int e = tid;
+        double xv[kMaxKS], gv[kMaxKS];
+        float pv[kMaxKS];
 #pragma unroll
-        for (int s = 0; s < kMaxKS; ++s) xv[s] = s < KS ? xn2[(size_t)s * T + t] : 0.0;
-        double xs2 = 0.0;
-#pragma unroll
-        for (int s = 0; s < kMaxKS; ++s) xs2 += xv[s];
-        const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
-        for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
-            float pv[kMaxKS];
-            double gv[kMaxKS];
+        for (int s = 0; s < kMaxKS; ++s) {
+            const bool in = s < KS && e < E;
+            xv[s] = s < KS ? xn2[(size_t)s * T + t] : 0.0;
+            pv[s] = in ? part[((size_t)s * T + t) * E + e] : 0.f;
+            gv[s] = in ? gn2[(size_t)s * E + e] : 0.0;
+        }
+        if (e < E) {
+            double xs2 = 0.0, gs2 = 0.0;
+            float lh = 0.f;
 #pragma unroll
             for (int s = 0; s < kMaxKS; ++s) {
-                pv[s] = s < KS ? part[((size_t)s * T + t) * E + e] : 0.f;
-                gv[s] = s < KS ? gn2[(size_t)s * E + e] : 0.0;
+                xs2 += xv[s];
+                gs2 += gv[s];
+                lh += pv[s];
             }
-            float lh = 0.f;
-            double gs2 = 0.0;
-#pragma unroll
-            for (int s = 0; s < kMaxKS; ++s) { lh += pv[s]; gs2 += gv[s]; }
+            const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
             const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
-            const double lo = (double)lh - beta;
-            s_lo[e] = lo;
             s_hi[e] = (double)lh + beta;
-            // rank key: lo rounded DOWN to fp32, made order-preserving as an
-            // unsigned integer, with the expert id below it (ties -> lower id first)
-            float lf = (float)lo;
-            uint32_t bits = __float_as_uint(lf);
-            if ((double)lf > lo)   // one fp32 step toward -inf (lo is finite)
-                bits = (lf > 0.0f) ? bits - 1u : (lf == 0.0f ? 0x80000001u : bits + 1u);
-            const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-            s_key[e] = ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+            s_key[e] = rank_key((double)lh - beta, e);
         }
     }
     __syncthreads();
-    // Candidate threshold: the k-th largest of the lower bounds rounded down to
-    // fp32 (keys in s_key).  It is <= the k-th largest exact lower bound, so the
-    // candidates it admits are a superset of the exact ones (all still re-scored
-    // in fp64).  An expert's rank is the number of keys above its own (keys are
-    // unique); the expert of rank k - 1 gives the threshold.
-    for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
-        const uint64_t key = s_key[e];
-        int rank = 0;
-        int f0 = 0;
-        for (; f0 + 16 <= E; f0 += 16) {
-            uint64_t w[16];
+    // Threshold: the k-th largest rank key (it is <= the k-th largest exact
+    // lower bound, so the candidates below are a superset of the exact ones).
+    if (wave == 0) {
+        uint64_t k16[kMaxExperts / 64];
 #pragma unroll
-            for (int q = 0; q < 16; ++q) w[q] = s_key[f0 + q];
+        for (int sl = 0; sl < kMaxExperts / 64; ++sl) {
+            const int e = lane + 64 * sl;
+            k16[sl] = e < E ? s_key[e] : 0;
+        }
+        uint64_t kth = 0;
+        for (int r = 0; r < topk; ++r) {
+            uint64_t m = 0;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) rank += (int)(w[q] > key);
+            for (int sl = 0; sl < kMaxExperts / 64; ++sl) m = k16[sl] > m ? k16[sl] : m;
+            kth = wave_max_u64(m);
+#pragma unroll
+            for (int sl = 0; sl < kMaxExperts / 64; ++sl) k16[sl] = k16[sl] == kth ? 0 : k16[sl];
         }
-        for (int f = f0; f < E; ++f) rank += (int)(s_key[f] > key);
-        if (rank == topk - 1) {
-            const uint32_t ord = (uint32_t)(key >> 32);
-            const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-            s_lowk = (double)__uint_as_float(bits);
-        }
+        if (lane == 0) s_lowk = key_value(kth);
     }
-    if (threadIdx.x == 0) s_ncand = 0;
     __syncthreads();
-    // candidates: every expert whose upper bound reaches lowk (the order of the
-    // list does not matter: the final ranking is by (score, id))
-    {
-        const double lowk = s_lowk;
-        for (int e = threadIdx.x; e < E; e += 64 * kSelWaves)
-            if (s_hi[e] >= lowk) s_cand[atomicAdd(&s_ncand, 1)] = e;
-    }
+    // candidates: every expert whose upper bound reaches the threshold
+    if (tid < E && s_hi[tid] >= s_lowk) s_cand[atomicAdd(&s_ncand, 1)] = tid;
     __syncthreads();
     const int nc = s_ncand;
-    // fp64 re-scoring of the candidates, kMaxCand at a time: item (c, s) =
-    // candidate c over K slice s of kSlices; the slice sums of a candidate are
-    // added in slice order by one thread, so the score is deterministic.
-    for (int cb = 0; cb < nc; cb += kMaxCand) {
-        const int ncb = min(kMaxCand, nc - cb);
-        for (int i0 = 0; i0 < ncb * kSlices; i0 += 64 * kSelWaves) {
-            const int i = i0 + threadIdx.x;
-            if (i < ncb * kSlices) {
-                const int c = i / kSlices, sl = i - c * kSlices;
-                const int len = d / kSlices, k0 = sl * len;
+    // fp64 re-scoring: item (c, sl) = candidate c over K slice sl.  nsl slices
+    // of len elements, len a multiple of 8 (one 16-byte load): nsl = the largest
+    // divisor of d / 8 up to kSlices; kSelThreads / nsl candidates per pass.
+    int nsl = kSlices;
+    while ((d / 8) % nsl) --nsl;
+    const int len = d / nsl, maxc = kSelThreads / nsl;
+    for (int cb = 0; cb < nc; cb += maxc) {
+        const int ncb = min(maxc, nc - cb);
+        {
+            const int c = tid / nsl, sl = tid - c * nsl;
+            if (c < ncb) {
+                const int k0 = sl * len;
                 const uint16_t* gx = xrow + k0;
                 const uint16_t* gg = G + (size_t)s_cand[cb + c] * d + k0;
                 double acc4[4] = {0.0, 0.0, 0.0, 0.0};   // four chains, added in a fixed order
@@ -265,20 +287,20 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
                         }
                     }
                 }
-                s_part[i] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+                s_part[tid] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
             }
         }
         __syncthreads();
-        for (int c = threadIdx.x; c < ncb; c += 64 * kSelWaves) {
+        if (tid < ncb) {
             double sc = 0.0;
-            for (int sl = 0; sl < kSlices; ++sl) sc += s_part[c * kSlices + sl];
-            s_score[cb + c] = sc;
+            for (int sl = 0; sl < nsl; ++sl) sc += s_part[tid * nsl + sl];
+            s_score[cb + tid] = sc;
         }
         __syncthreads();
     }
     // top-k among candidates by (fp64 score desc, id asc): a candidate's rank is
     // the number of candidates ahead of it; ranks 0..k-1 are the selected slots
-    for (int c = threadIdx.x; c < nc; c += 64 * kSelWaves) {
+    for (int c = tid; c < nc; c += kSelThreads) {
         const double v = s_score[c];
         const int id = s_cand[c];
         int rank = 0;
@@ -324,16 +346,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void router_select_kernel(
 constexpr int kWTok = 4;            // tokens (waves) per workgroup
 constexpr int kWGroup = 8;          // candidates scored together
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-        const uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
-}
-
 template <int kWSlots>
 __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
@@ -373,13 +385,8 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
                 gs2 += gn2[(size_t)s * E + e];
             }
             const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
-            const double lo = (double)lh - beta;
             hi[sl] = (double)lh + beta;
-            float lf = (float)lo;
-            uint32_t bits = __float_as_uint(lf);
-            if ((double)lf > lo) bits = (lf > 0.0f) ? bits - 1u : (lf == 0.0f ? 0x80000001u : bits + 1u);
-            const uint32_t ord = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-            key[sl] = ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+            key[sl] = rank_key((double)lh - beta, e);
         }
     }
 
@@ -393,8 +400,7 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
 #pragma unroll
         for (int sl = 0; sl < kWSlots; ++sl) key[sl] = key[sl] == kth ? 0 : key[sl];
     }
-    const uint32_t kord = (uint32_t)(kth >> 32);
-    const double lowk = (double)__uint_as_float((kord & 0x80000000u) ? (kord & 0x7FFFFFFFu) : ~kord);
+    const double lowk = key_value(kth);
 
     // ---- candidates in ascending id order ----
     int nc = 0;
@@ -675,7 +681,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     } else {
         // few tokens: a workgroup per token (latency)
         dim3 g2(a.T);
-        hipLaunchKernelGGL(router_select_kernel, g2, dim3(64 * kSelWaves), 0, s, a.X, a.G, a.part, a.xn2,
+        hipLaunchKernelGGL(router_select_kernel, g2, dim3(kSelThreads), 0, s, a.X, a.G, a.part, a.xn2,
                            a.gn2, a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
     }
     return hipGetLastError();
