@@ -146,14 +146,27 @@ constexpr int kSlices = 64;         // at most this many K slices of one fp64 ca
 constexpr int kSelThreads = 1024;
 constexpr int kWideSelectTokens = 1024;   // from here on, one wave per token
 
+// Wave-wide unsigned max through DPP row shifts and row broadcasts (lanes that
+// read outside their row get 0, the identity): after the row_shr steps lane 15
+// of each row holds the row's max, row_bcast15 / row_bcast31 carry it up to lane
+// 63, which readlane then hands to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));   // row_shr:1
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));   // row_shr:2
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));   // row_shr:4
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));   // row_shr:8
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Wave-wide max of 64-bit keys: the max of the high words, then the max of the
+// low words among the lanes that hold that high word.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)v, o, 64), hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-        const uint64_t w = ((uint64_t)hi << 32) | lo;
-        v = w > v ? w : v;
-    }
-    return v;
+    const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Rank key of a lower bound: lo rounded DOWN to fp32, made order-preserving as
@@ -174,6 +187,7 @@ __device__ __forceinline__ double key_value(uint64_t key) {
     return (double)__uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
 }
 
+template <int EPL>   // experts per lane of wave 0 in the tournament: 64 EPL >= E
 __global__ __launch_bounds__(kSelThreads) void router_select_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
@@ -229,20 +243,22 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(
     // Threshold: the k-th largest rank key (it is <= the k-th largest exact
     // lower bound, so the candidates below are a superset of the exact ones).
     if (wave == 0) {
-        uint64_t k16[kMaxExperts / 64];
+        // lane's keys (experts lane + 64 sl) in registers; k rounds of a wave max,
+        // the owner of each maximum dropping it
+        uint64_t key[EPL];
 #pragma unroll
-        for (int sl = 0; sl < kMaxExperts / 64; ++sl) {
+        for (int sl = 0; sl < EPL; ++sl) {
             const int e = lane + 64 * sl;
-            k16[sl] = e < E ? s_key[e] : 0;
+            key[sl] = e < E ? s_key[e] : 0;
         }
         uint64_t kth = 0;
         for (int r = 0; r < topk; ++r) {
             uint64_t m = 0;
 #pragma unroll
-            for (int sl = 0; sl < kMaxExperts / 64; ++sl) m = k16[sl] > m ? k16[sl] : m;
+            for (int sl = 0; sl < EPL; ++sl) m = key[sl] > m ? key[sl] : m;
             kth = wave_max_u64(m);
 #pragma unroll
-            for (int sl = 0; sl < kMaxExperts / 64; ++sl) k16[sl] = k16[sl] == kth ? 0 : k16[sl];
+            for (int sl = 0; sl < EPL; ++sl) key[sl] = key[sl] == kth ? 0 : key[sl];
         }
         if (lane == 0) s_lowk = key_value(kth);
     }
@@ -292,9 +308,10 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(
         }
         __syncthreads();
         if (tid < ncb) {
-            double sc = 0.0;
-            for (int sl = 0; sl < nsl; ++sl) sc += s_part[tid * nsl + sl];
-            s_score[cb + tid] = sc;
+            // slices dealt round-robin to four chains, combined in a fixed order
+            double c4[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int sl = 0; sl < nsl; ++sl) c4[sl & 3] += s_part[tid * nsl + sl];
+            s_score[cb + tid] = (c4[0] + c4[1]) + (c4[2] + c4[3]);
         }
         __syncthreads();
     }
@@ -681,8 +698,12 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     } else {
         // few tokens: a workgroup per token (latency)
         dim3 g2(a.T);
-        hipLaunchKernelGGL(router_select_kernel, g2, dim3(kSelThreads), 0, s, a.X, a.G, a.part, a.xn2,
-                           a.gn2, a.T, a.E, a.d, KS, a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+        auto k = a.E <= 128 ? router_select_kernel<2>
+                 : a.E <= 320 ? router_select_kernel<5>
+                 : a.E <= 512 ? router_select_kernel<8>
+                              : router_select_kernel<kMaxExperts / 64>;
+        hipLaunchKernelGGL(k, g2, dim3(kSelThreads), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
+                           a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
     }
     return hipGetLastError();
 }
