@@ -25,7 +25,7 @@
 // dequantize-then-MFMA.
 //
 // GEMM1 epilogue: a = silu(gate) * up (rows [0,F) of w13 gate, [F,2F) up), bf16;
-// W4A4 quantize-dequantizes a per 16 columns.  GEMM2: Y = acc * g2 (fp32 rows).
+// W4A4 quantize-dequantizes a per 16 columns.  GEMM2: Y = acc * g2 (bf16 rows).
 // Layer semantics: the page "Serving Solar Open 2 on DGX Spark", sections "수정
 // 사항 › b12x에서의 Expert Parallelism 구현 추가" and "b12x 버전이 실제 NVFP4
 // 체크포인트를 읽어들이도록 만들기".
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
         for (int tg = 0; tg < TGM; ++tg) {
             const float y = dec_result<TGM, 1>(acc, tg, 0, g);
             const int r = tl.rb + tg * 4 + g;
-            if (r < tl.re) a.Y[(size_t)r * d + col] = y * g2;
+            if (r < tl.re) a.Y[(size_t)r * d + col] = (uint16_t)f32_to_bf16_rne(y * g2);
         }
     };
     dec_stream<1, TGM, DEPTH, RGS, FULLA, SEG>(s_arow, ntok, F, codes, scales, cstride, sstride, lds, epi);

@@ -114,7 +114,7 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     const bool w4a4 = p.mode == MOE_NVFP4_W4A4;
     pl.hq = take(w4a4 ? T * d * 2 : 0);
     pl.act = take(pl.rows * F * 2);
-    pl.Y = take(pl.rows * d * 4);
+    pl.Y = take(pl.rows * d * 2);
     pl.total = o;
 }
 
@@ -296,7 +296,7 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     g.local = to_internal(local);
     g.shared = to_internal(p->has_shared ? shared : nullptr);
     g.act = at<uint16_t>(workspace, pl.act);
-    g.Y = at<float>(workspace, pl.Y);
+    g.Y = at<uint16_t>(workspace, pl.Y);
     const bool dec = pl.path == MOE_NVFP4_PATH_DECODE;
     if ((st = hip_status(dec ? moe::launch_dec_gemm1(g, s) : moe::launch_gemm1(g, pl.path, s), "gemm1 launch")))
         return st;

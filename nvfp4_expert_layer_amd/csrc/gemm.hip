@@ -17,27 +17,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (idx >= (long long)a.T * per_row) return;
     const int t = (int)(idx / per_row), c0 = (int)(idx % per_row) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto add_row = [&](size_t row, float w) {
+        const u32x4_t y = *reinterpret_cast<const u32x4_t*>(a.Y + row * a.d + c0);
+        const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s[2 * q] = fmaf(w, bf16_bits_to_f32(yw[q] & 0xFFFFu), s[2 * q]);
+            s[2 * q + 1] = fmaf(w, bf16_bits_to_f32(yw[q] >> 16), s[2 * q + 1]);
+        }
+    };
     for (int j = 0; j < a.topk; ++j) {
         const int row = a.inv[(size_t)t * a.topk + j];
-        if (row < 0) continue;
-        const float w = a.topk_w[(size_t)t * a.topk + j];
-        const f32x4_t* y = reinterpret_cast<const f32x4_t*>(a.Y + (size_t)row * a.d + c0);
-        f32x4_t y0 = y[0], y1 = y[1];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s[q] = fmaf(w, y0[q], s[q]);
-            s[4 + q] = fmaf(w, y1[q], s[4 + q]);
-        }
+        if (row >= 0) add_row((size_t)row, a.topk_w[(size_t)t * a.topk + j]);
     }
-    if (a.has_shared) {
-        const f32x4_t* y = reinterpret_cast<const f32x4_t*>(a.Y + ((size_t)a.T * a.topk + t) * a.d + c0);
-        f32x4_t y0 = y[0], y1 = y[1];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s[q] += y0[q];
-            s[4 + q] += y1[q];
-        }
-    }
+    if (a.has_shared) add_row((size_t)a.T * a.topk + t, 1.0f);
     u32x4_t o;
     o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
     o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);

@@ -49,14 +49,14 @@ struct GemmArgs {
     const uint16_t* hq;           // W4A4: hidden NVFP4-quantized, exact dequantized bf16 [T][d]
     ExpertWeights local, shared;
     uint16_t* act;                // SwiGLU output bf16 [R][F] (W4A4: exact dequantized NVFP4 values)
-    float* Y;                     // fp32 [R][d];  R = T*k + T
+    uint16_t* Y;                  // expert outputs, bf16 [R][d];  R = T*k + T
 };
 
 struct CombineArgs {
     int T, d, topk, has_shared;
     const float* topk_w;          // [T][k]
     const int32_t* inv;           // [T][k] row of each pair, -1 dropped
-    const float* Y;               // [R][d]
+    const uint16_t* Y;            // bf16 [R][d]
     uint16_t* out;                // bf16 [T][d]
 };
 

@@ -25,7 +25,7 @@
 // the same up columns, so the SwiGLU a = silu(g13*gate) * (g13*up) is formed
 // in registers; W4A4 quantize-dequantizes a per 16 columns (16 lanes).  Stored
 // bf16.
-// GEMM2 (KIND 2): Y = g2 * acc, fp32 rows.
+// GEMM2 (KIND 2): Y = g2 * acc, bf16 rows (through LDS, 16-byte stores).
 //
 // Workgroups are mapped so that each of the 8 XCDs (hardware workgroup b runs on
 // XCD b % 8) takes a contiguous range of (tile, column block) pairs, tile-major:
@@ -333,22 +333,36 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
         }
         return;
     }
-    if (!colv) return;
-    const int lr = (lane >> 5) * 4;                       // row offset of this lane within an 8-row group
-    {
+    // GEMM2: Y = g2 * acc in bf16, through LDS (bf16 [256][264]: the two
+    // half-waves' rows land half a bank period apart) so that each thread
+    // writes whole 16-byte pieces of rows
+    constexpr int YS = 264;                               // row stride (bf16 elements)
+    uint16_t* Ys = reinterpret_cast<uint16_t*>(smem);
+    __syncthreads();                                      // every wave's direct loads have landed
+    const int lr = (lane >> 5) * 4;
+    if (colv) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (i >= nvi) break;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int col = nt * kPN + wn * 32 * NJ + j * 32 + (lane & 31);
+                const int col = wn * 32 * NJ + j * 32 + (lane & 31);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int row = rb + wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
-                    if (row < re) a.Y[(size_t)row * d + col] = acc[i][j][v] * gscale;
+                    const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                    Ys[row * YS + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * gscale);
                 }
             }
         }
+    }
+    __syncthreads();
+    const int nrow = re - rb, ncol = min(kPN, d - nt * kPN);
+    for (int pc = tid; pc < kPM * (kPN / 8); pc += 64 * WAVES) {
+        const int row = pc >> 5, c8 = (pc & 31) * 8;
+        if (row >= nrow) break;                           // rows grow with pc
+        if (c8 < ncol)
+            *reinterpret_cast<u32x4_t*>(a.Y + (size_t)(rb + row) * d + nt * kPN + c8) =
+                *reinterpret_cast<const u32x4_t*>(Ys + row * YS + c8);
     }
 }
 
