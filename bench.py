@@ -281,7 +281,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8)
+    ap.add_argument("--cpu-sample", type=int, default=48,
+                    help="tokens of the headline batch the CPU oracle is timed on (~10-30 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hashes and exit")
