@@ -13,6 +13,7 @@ headline workload (the T=64 expert-shard decode step), with:
              prefill): algorithmic bytes (or flops) per launch / the kernel's
              average duration from the two HIP events recorded around it in each
              timed step (the per-stage breakdown comes from a separate pass)
+  graph_replay  the same forward captured once in a HIP graph, K replays timed
   secondary  the same for the T=8192 all-expert W4A4 prefill step
   cpu_baseline  the CPU oracle timed on a bounded sample of the headline workload
 --all prints one line per workload instead (a report, not the default line).
@@ -182,6 +183,20 @@ def bench_workload(name, steps, warmup, hip):
     elapsed = time.perf_counter() - t0
     g1_ms = sum(hip.elapsed_ms(g1ev[2 * s], g1ev[2 * s + 1]) for s in range(steps)) / steps
     hip.destroy(g1ev)
+    # the same forward captured once in a HIP graph and replayed K times (a
+    # deployment that removes the host launch gaps); reported beside `value`
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_s = time.perf_counter() - tg
+    del graph
     # per-stage breakdown from a separate, untimed pass with all six events
     nb = min(steps, 10)
     evs = hip.create(6 * nb)
@@ -214,6 +229,7 @@ def bench_workload(name, steps, warmup, hip):
     layer_hbm_frac = alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3)
     layer_mfma_frac = alg["layer_flops"] / (BF16_PEAK_TFLOPS * 1e12) / (ms * 1e-3)
     res = {"workload": name, "tokens_per_s": w.T * steps / elapsed, "ms_per_step": ms,
+           "graph_tokens_per_s": w.T * steps / graph_s, "graph_ms_per_step": graph_s * 1e3 / steps,
            "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
            "roofline": roof, "layer_hbm_frac": round(layer_hbm_frac, 4),
            "layer_mfma_frac": round(layer_mfma_frac, 4),
@@ -312,13 +328,17 @@ def main():
                 "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": "synthetic (seeded bf16 draws, NVFP4-quantized on the GPU)", "config": config_of(w),
-                "roofline": r["roofline"], "layer_hbm_frac": r["layer_hbm_frac"],
+                "roofline": r["roofline"], "graph_replay": {"tokens_per_s": round(r["graph_tokens_per_s"], 1),
+                                                            "ms_per_step": round(r["graph_ms_per_step"], 4)},
+                "layer_hbm_frac": r["layer_hbm_frac"],
                 "layer_mfma_frac": r["layer_mfma_frac"], "stage_us": r["stage_us"],
                 "touched_experts": r["touched_experts"], "local_pairs": r["local_pairs"]}
         if not args.all and not args.no_secondary and name != SECONDARY:
             w2, r2 = bench_workload(SECONDARY, max(5, args.steps // 5), args.warmup, hip)
             line["secondary"] = {"config": config_of(w2), "tokens_per_s": round(r2["tokens_per_s"], 1),
                                  "ms_per_step": round(r2["ms_per_step"], 4), "roofline": r2["roofline"],
+                                 "graph_replay": {"tokens_per_s": round(r2["graph_tokens_per_s"], 1),
+                                                  "ms_per_step": round(r2["graph_ms_per_step"], 4)},
                                  "layer_mfma_frac": r2["layer_mfma_frac"], "stage_us": r2["stage_us"]}
         if cpu is not None and (not args.all or name == HEADLINE):
             line["cpu_baseline"] = cpu

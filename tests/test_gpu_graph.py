@@ -1,0 +1,70 @@
+"""The forward enqueues only kernels (no allocation, no host synchronisation, no
+memset nodes), so a caller can capture it in a HIP graph.  A captured forward is
+replayed several times, with the inputs rewritten by eager work between the
+replays; every replay must equal the eager forward on the same inputs bit for
+bit (the kernels are deterministic)."""
+import pytest
+import torch
+
+import nvfp4_expert_layer_amd as nv
+import workloads
+from tests.gpu_helpers import Layer, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+W4A16, W4A4 = workloads.W4A16, workloads.W4A4
+
+MID = workloads.Workload("mid_graph", T=200, d=512, F=256, E=24, k=4, offset=0, L=24, has_shared=True,
+                         mode=W4A16, hidden_seed=17, gate_seed=17, weight_seed=17, gate_std=0.05)
+
+
+def _graph_vs_eager(lay, offset, L, shared, mode, path, n_replays=3):
+    w = lay.w
+    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, offset, L, shared, mode, path)
+    ws = nv.alloc_workspace(p)
+    local = lay.local_weights(offset, L)
+    sh = lay.shared if shared else None
+    x = lay.x.clone()
+    out = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
+    # eager first (one-time set-up happens outside the capture)
+    nv.moe_nvfp4_forward(p, x, lay.gate_w, local, sh, ws, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nv.moe_nvfp4_forward(p, x, lay.gate_w, local, sh, ws, out)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    for r in range(n_replays):
+        gen.manual_seed(1000 + r)
+        new_x = torch.randn(w.T, w.d, generator=gen, device="cuda").to(torch.bfloat16)
+        if r == 1:
+            new_x[3] = 0                                   # a zero token in one replay
+        x.copy_(new_x)                                     # eager work between replays
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = torch.empty_like(out)
+        ws2 = nv.alloc_workspace(p)
+        nv.moe_nvfp4_forward(p, new_x, lay.gate_w, local, sh, ws2, ref)
+        torch.cuda.synchronize()
+        assert not torch.isnan(got).any().item(), f"replay {r} left NaNs"
+        assert torch.equal(got, ref), f"replay {r} differs from the eager forward"
+    return True
+
+
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
+def test_graph_replays_match_eager_mid(mode, path):
+    require_gpu()
+    lay = Layer(MID)
+    log(f"graph replay mid mode={mode} path={path}")
+    _graph_vs_eager(lay, 4, 16, True, mode, path)
+
+
+def test_graph_replays_match_eager_decode_shard():
+    require_gpu()
+    w = workloads.WORKLOADS["decode_shard0_w4a16"]
+    lay = Layer(w, experts_range=(0, w.L))
+    log("graph replay decode shard T=64")
+    _graph_vs_eager(lay, w.offset, w.L, True, w.mode, nv.PATH_AUTO)
