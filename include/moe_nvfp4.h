@@ -179,6 +179,50 @@ int moe_nvfp4_quantize_weights(const void *w, int32_t n, int32_t R, int32_t C, u
 int moe_nvfp4_quantize_activations(const void *x, int32_t R, int32_t C, uint8_t *codes,
                                    uint8_t *scales, void *stream);
 
+/* Checkpoint preparation (the page "Serving Solar Open 2 on DGX Spark", section
+ * "b12x 버전이 실제 NVFP4 체크포인트를 읽어들이도록 만들기": pre-quantized NVFP4
+ * checkpoints hold packed FP4 weights, FP8 block scales and per-expert global
+ * scales, in one of two conventions for the global scale; the loader reads
+ * either, handles the fused gate/up row order and slices the scales of an
+ * expert shard).  The prepared tensors are the layout moe_nvfp4_weights
+ * describes.
+ *
+ * Global scale conventions of a checkpoint tensor:
+ *   MULTIPLIER  w = e2m1 * e4m3 * g          (g stored as is)
+ *   INVERSE     w = e2m1 * e4m3 / g_stored   (prepared g = fp32(1 / g_stored),
+ *                                             one correctly rounded division)
+ * Gate/up row order of a checkpoint's fused w13:
+ *   GATE_UP     rows [0, F) gate, [F, 2F) up  (copied as is)
+ *   UP_GATE     rows [0, F) up,   [F, 2F) gate (the two halves are swapped)
+ * Codes and block scales are copied bit for bit (no re-rounding). */
+typedef enum { MOE_NVFP4_GLOBAL_MULTIPLIER = 0, MOE_NVFP4_GLOBAL_INVERSE = 1 } moe_nvfp4_global_convention;
+typedef enum { MOE_NVFP4_GATE_UP = 0, MOE_NVFP4_UP_GATE = 1 } moe_nvfp4_w13_order;
+
+/* A checkpoint's expert tensors (device pointers; num_experts experts,
+ * expert-major, the moe_nvfp4_weights shapes, w13 in w13_order). */
+typedef struct {
+    const uint8_t *w13;         /* [E][2F][d/2]                                     */
+    const uint8_t *w13_scale;   /* [E][2F][d/16]                                    */
+    const float   *w13_global;  /* [E] in global_convention                          */
+    const uint8_t *w2;          /* [E][d][F/2]                                      */
+    const uint8_t *w2_scale;    /* [E][d][F/16]                                     */
+    const float   *w2_global;   /* [E] in global_convention                          */
+    int32_t num_experts, d_model, d_ff;
+    int32_t global_convention;  /* moe_nvfp4_global_convention                        */
+    int32_t w13_order;          /* moe_nvfp4_w13_order                                */
+} moe_nvfp4_checkpoint;
+
+/* Writes experts [first_expert, first_expert + count) of `ck` into `dst`
+ * (caller-owned device tensors for `count` experts, the moe_nvfp4_weights
+ * layout; they must not overlap the checkpoint's).  d_model and d_ff follow the
+ * forward's rules; 0 <= first_expert, first_expert + count <= num_experts,
+ * count <= 65535 (count == 0 enqueues nothing); pointers as in the forward
+ * (16-byte aligned codes and scales, 4-byte aligned globals).  Enqueued on
+ * `stream`; returns INVALID_ARG / UNSUPPORTED_SHAPE before enqueuing anything,
+ * ARCH when the current device is not gfx950, HIP when a launch fails. */
+int moe_nvfp4_prepare(const moe_nvfp4_checkpoint *ck, int32_t first_expert, int32_t count,
+                      const moe_nvfp4_weights *dst, void *stream);
+
 /* Static description of a status code. */
 const char *moe_nvfp4_strerror(int status);
 

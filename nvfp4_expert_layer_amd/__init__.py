@@ -44,6 +44,16 @@ class moe_nvfp4_weights(ctypes.Structure):
         "w13", "w13_scale", "w13_global", "w2", "w2_scale", "w2_global")]
 
 
+GLOBAL_MULTIPLIER, GLOBAL_INVERSE = 0, 1
+GATE_UP, UP_GATE = 0, 1
+
+
+class moe_nvfp4_checkpoint(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w13", "w13_scale", "w13_global", "w2", "w2_scale", "w2_global")] + [
+        (n, ctypes.c_int32) for n in ("num_experts", "d_model", "d_ff", "global_convention", "w13_order")]
+
+
 _lib = None
 
 
@@ -67,12 +77,13 @@ def lib():
         L.moe_nvfp4_route.argtypes = [P(moe_nvfp4_problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_nvfp4_quantize_weights.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.moe_nvfp4_quantize_activations.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_nvfp4_prepare.argtypes = [P(moe_nvfp4_checkpoint), i32, i32, P(moe_nvfp4_weights), vp]
         L.moe_nvfp4_strerror.argtypes = [ctypes.c_int]
         L.moe_nvfp4_strerror.restype = ctypes.c_char_p
         L.moe_nvfp4_last_error.argtypes = []
         L.moe_nvfp4_last_error.restype = ctypes.c_char_p
         for f in ("workspace_size", "validate", "forward", "forward_timed", "route", "quantize_weights",
-                  "quantize_activations"):
+                  "quantize_activations", "prepare"):
             getattr(L, "moe_nvfp4_" + f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -129,6 +140,23 @@ class NVFP4Experts:
                             torch.empty(n, dtype=torch.float32, device=device),
                             torch.empty(n, d, F // 2, **u8), torch.empty(n, d, F // 16, **u8),
                             torch.empty(n, dtype=torch.float32, device=device))
+
+
+def moe_nvfp4_prepare(ck, global_convention, w13_order, first_expert, count, dst, stream=None):
+    """Checkpoint tensors `ck` (an NVFP4Experts holding a checkpoint's E experts,
+    w13 in `w13_order`, global scales in `global_convention`) -> experts
+    [first_expert, first_expert + count) written into `dst` (an NVFP4Experts of
+    count experts, the kernel layout)."""
+    for part in (ck, dst):
+        for t in (part.w13, part.w13_scale, part.w13_global, part.w2, part.w2_scale, part.w2_global):
+            _ptr(t)   # on the GPU and contiguous
+    E, twoF, dh = ck.w13.shape
+    c = moe_nvfp4_checkpoint(*(t.data_ptr() for t in (ck.w13, ck.w13_scale, ck.w13_global, ck.w2, ck.w2_scale,
+                                                      ck.w2_global)),
+                             E, dh * 2, twoF // 2, global_convention, w13_order)
+    dw = dst.c_struct()
+    _check(lib().moe_nvfp4_prepare(ctypes.byref(c), first_expert, count, ctypes.byref(dw), _stream(stream)))
+    return dst
 
 
 def moe_nvfp4_strerror(status):

@@ -380,4 +380,64 @@ int moe_nvfp4_quantize_activations(const void* x, int32_t R, int32_t C, uint8_t*
     return st ? st : ok();
 }
 
+int moe_nvfp4_prepare(const moe_nvfp4_checkpoint* ck, int32_t first_expert, int32_t count,
+                      const moe_nvfp4_weights* dst, void* stream) {
+    if (!ck || !dst) return fail(MOE_NVFP4_ERR_INVALID_ARG, "checkpoint or destination is NULL");
+    const int d = ck->d_model, F = ck->d_ff;
+    if (d < 128 || d > 16384 || d % 128)
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_model %d: need a multiple of 128 in 128..16384", d);
+    if (F < 128 || F > 16384 || F % 128)
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_ff %d: need a multiple of 128 in 128..16384", F);
+    if (ck->global_convention != MOE_NVFP4_GLOBAL_MULTIPLIER && ck->global_convention != MOE_NVFP4_GLOBAL_INVERSE)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown global scale convention %d", ck->global_convention);
+    if (ck->w13_order != MOE_NVFP4_GATE_UP && ck->w13_order != MOE_NVFP4_UP_GATE)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown w13 row order %d", ck->w13_order);
+    if (ck->num_experts < 1 || first_expert < 0 || count < 0 || (long long)first_expert + count > ck->num_experts)
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "experts [%d, %d) outside the checkpoint's %d", first_expert,
+                    first_expert + count, ck->num_experts);
+    if (count > 65535) return fail(MOE_NVFP4_ERR_INVALID_ARG, "count %d: at most 65535 experts per call", count);
+    int st;
+    const moe_nvfp4_weights src = {ck->w13, ck->w13_scale, ck->w13_global, ck->w2, ck->w2_scale, ck->w2_global};
+    if ((st = check_weights(&src, "checkpoint"))) return st;
+    if ((st = check_weights(dst, "destination"))) return st;
+    // per-expert sizes of the six tensors; destination ranges must not overlap the sources
+    const size_t b13 = (size_t)2 * F * (d / 2), s13 = (size_t)2 * F * (d / 16);
+    const size_t b2 = (size_t)d * (F / 2), s2 = (size_t)d * (F / 16);
+    auto overlap = [&](const void* a, const void* b, size_t na, size_t nb) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+        return x < y + nb && y < x + na;
+    };
+    const size_t n = (size_t)count, E = (size_t)ck->num_experts;
+    if (overlap(dst->w13, ck->w13, n * b13, E * b13) || overlap(dst->w13_scale, ck->w13_scale, n * s13, E * s13) ||
+        overlap(dst->w2, ck->w2, n * b2, E * b2) || overlap(dst->w2_scale, ck->w2_scale, n * s2, E * s2) ||
+        overlap(dst->w13_global, ck->w13_global, n * 4, E * 4) || overlap(dst->w2_global, ck->w2_global, n * 4, E * 4))
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "destination overlaps the checkpoint");
+    int dev;
+    if ((st = current_arch_ok(&dev))) return st;
+    if (count == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t f = (size_t)first_expert;
+    const bool swap = ck->w13_order == MOE_NVFP4_UP_GATE, inv = ck->global_convention == MOE_NVFP4_GLOBAL_INVERSE;
+    uint8_t* d13 = const_cast<uint8_t*>(dst->w13);
+    uint8_t* d13s = const_cast<uint8_t*>(dst->w13_scale);
+    uint8_t* d2 = const_cast<uint8_t*>(dst->w2);
+    uint8_t* d2s = const_cast<uint8_t*>(dst->w2_scale);
+    if ((st = hip_status(moe::launch_prepare_rows(ck->w13 + f * b13, d13, count, 2 * F, d / 2, swap, s),
+                         "prepare w13 codes")) ||
+        (st = hip_status(moe::launch_prepare_rows(ck->w13_scale + f * s13, d13s, count, 2 * F, d / 16, swap, s),
+                         "prepare w13 scales")) ||
+        (st = hip_status(moe::launch_prepare_rows(ck->w2 + f * b2, d2, count, d, F / 2, false, s),
+                         "prepare w2 codes")) ||
+        (st = hip_status(moe::launch_prepare_rows(ck->w2_scale + f * s2, d2s, count, d, F / 16, false, s),
+                         "prepare w2 scales")) ||
+        (st = hip_status(moe::launch_prepare_global(ck->w13_global + f, const_cast<float*>(dst->w13_global), count,
+                                                    inv, s),
+                         "prepare w13 global")) ||
+        (st = hip_status(moe::launch_prepare_global(ck->w2_global + f, const_cast<float*>(dst->w2_global), count,
+                                                    inv, s),
+                         "prepare w2 global")))
+        return st;
+    return ok();
+}
+
 }  // extern "C"

@@ -69,6 +69,9 @@ hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out,
 hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_prepare_rows(const uint8_t* src, uint8_t* dst, int n, int rows, int row_bytes, bool swap_halves,
+                               hipStream_t s);
+hipError_t launch_prepare_global(const float* src, float* dst, int n, bool inverse, hipStream_t s);
 int gemm_bm(int path, int T, int topk, int E);   // rows per tile of the chosen path
 int pf_rows();                                    // rows per tile of the prefill GEMMs
 int dec_rows(int T, int topk, int E);

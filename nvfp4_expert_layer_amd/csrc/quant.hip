@@ -167,4 +167,48 @@ hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Checkpoint preparation: expert tensors copied 4 bytes at a time, the two row
+// halves of each expert optionally swapped (fused w13 stored up-then-gate), and
+// global scales taken as they are or inverted (one correctly rounded fp32
+// division).  The page "Serving Solar Open 2 on DGX Spark", section "b12x 버전이
+// 실제 NVFP4 체크포인트를 읽어들이도록 만들기".
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prepare_rows_kernel(const uint32_t* __restrict__ src,
+                                                           uint32_t* __restrict__ dst, int rows, int row_words,
+                                                           int swap_halves) {
+    const size_t per_expert = (size_t)rows * row_words;
+    const size_t e = blockIdx.y;
+    const uint32_t* s = src + e * per_expert;
+    uint32_t* o = dst + e * per_expert;
+    const int half = rows / 2;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_expert; i += (size_t)gridDim.x * 256) {
+        const int r = (int)(i / row_words), c = (int)(i - (size_t)r * row_words);
+        const int sr = swap_halves ? (r < half ? r + half : r - half) : r;
+        o[i] = s[(size_t)sr * row_words + c];
+    }
+}
+
+__global__ void prepare_global_kernel(const float* __restrict__ src, float* __restrict__ dst, int n, int inverse) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = inverse ? __fdiv_rn(1.0f, src[i]) : src[i];
+}
+
+hipError_t launch_prepare_rows(const uint8_t* src, uint8_t* dst, int n, int rows, int row_bytes, bool swap_halves,
+                               hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const size_t words = (size_t)rows * (row_bytes / 4);
+    const size_t blocks = (words + 255) / 256;
+    const unsigned gx = (unsigned)(blocks < 1024 ? blocks : 1024);
+    hipLaunchKernelGGL(prepare_rows_kernel, dim3(gx, n), dim3(256), 0, s, reinterpret_cast<const uint32_t*>(src),
+                       reinterpret_cast<uint32_t*>(dst), rows, row_bytes / 4, swap_halves ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare_global(const float* src, float* dst, int n, bool inverse, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prepare_global_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n, inverse ? 1 : 0);
+    return hipGetLastError();
+}
+
 }  // namespace moe

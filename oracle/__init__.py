@@ -31,10 +31,13 @@ Modules:
   moe     - router, shard filter, permutation, layer forward (vectorised).
   brute   - the same layer as plain per-token / per-expert Python loops, with
             its own decoding by formula, used to pin `moe` on tiny inputs.
+  checkpoint - preparation of pre-quantized checkpoints (global-scale
+            convention, gate/up row order, shard slicing), section "b12x 버전이
+            실제 NVFP4 체크포인트를 읽어들이도록 만들기".
 
 Parity status: every function here is pinned by a CPU test against the format
 definitions, closed forms, invariants or brute force (tests/test_oracle_*.py).
 End-to-end values at the workload sizes have no printed worked example on the
 pages; they are pinned only through those invariants.
 """
-from . import nvfp4, moe, brute  # noqa: F401
+from . import nvfp4, moe, brute, checkpoint  # noqa: F401
