@@ -40,8 +40,10 @@
  * W4A4 activations use the same element/scale format with no global scale:
  * scale = E4M3_rne_saturating(block_amax / 6), code = E2M1_rne_saturating(x / scale).
  *
- * Numerics: code * scale is exact in bf16; the GEMMs run on bf16 MFMA with fp32
- * accumulation and apply the fp32 global scale after accumulation.  Routing is
+ * Numerics: code * scale is exact in bf16 (and in f16); the GEMMs run on bf16
+ * MFMA (W4A16) or f16 MFMA on the tiled path in W4A4, where both operands are
+ * such products, with fp32 accumulation, and apply the fp32 global scale after
+ * accumulation.  Routing is
  * exact: bf16-MFMA logits carry a rigorous error bound, and every expert that
  * could be on either side of the top-k boundary is re-scored in fp64.
  *
@@ -86,7 +88,10 @@ typedef enum {
 
 /* Kernel path.  AUTO picks from the expected number of local pairs per local
  * expert, T * top_k / num_experts (the shard's expected load, not the global
- * one): weight-streaming kernels when it is small, tiled kernels otherwise. */
+ * one): weight-streaming kernels up to 6 (W4A16) or 2 (W4A4 with d and F
+ * multiples of 256, whose tiled kernels move the activations as NVFP4), tiled
+ * kernels above.  Both paths give results within the stated tolerances; they
+ * are not bit-identical to each other. */
 typedef enum {
     MOE_NVFP4_PATH_AUTO = 0,
     MOE_NVFP4_PATH_DECODE = 1,
@@ -127,6 +132,11 @@ int moe_nvfp4_workspace_size(const moe_nvfp4_problem *p, size_t *bytes);
  * Returns the status moe_nvfp4_forward would return for these arguments
  * (given non-null tensor pointers). */
 int moe_nvfp4_validate(const moe_nvfp4_problem *p, size_t workspace_bytes, const char *arch);
+
+/* The kernel path moe_nvfp4_forward takes for `p` (PATH_DECODE or
+ * PATH_PREFILL: AUTO resolved by the rule above).  Device-free.  Writes it to
+ * *path and returns OK, or INVALID_ARG / UNSUPPORTED_SHAPE for a bad problem. */
+int moe_nvfp4_resolved_path(const moe_nvfp4_problem *p, int32_t *path);
 
 /* The fused layer: out = this shard's partial sum (bf16 [T][d], fully
  * overwritten; a token with no local pair gets the shared term or 0).

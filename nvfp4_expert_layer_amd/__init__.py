@@ -69,6 +69,7 @@ def lib():
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.moe_nvfp4_workspace_size.argtypes = [P(moe_nvfp4_problem), P(sz)]
         L.moe_nvfp4_validate.argtypes = [P(moe_nvfp4_problem), sz, ctypes.c_char_p]
+        L.moe_nvfp4_resolved_path.argtypes = [P(moe_nvfp4_problem), P(i32)]
         L.moe_nvfp4_forward.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
                                         P(moe_nvfp4_weights), vp, sz, vp, vp]
         L.moe_nvfp4_forward_timed.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
@@ -171,6 +172,13 @@ def moe_nvfp4_workspace_size(problem):
     n = ctypes.c_size_t(0)
     _check(lib().moe_nvfp4_workspace_size(ctypes.byref(problem), ctypes.byref(n)))
     return n.value
+
+
+def moe_nvfp4_resolved_path(problem):
+    """PATH_DECODE or PATH_PREFILL: the path the forward takes for `problem`."""
+    out = ctypes.c_int32(0)
+    _check(lib().moe_nvfp4_resolved_path(ctypes.byref(problem), ctypes.byref(out)))
+    return out.value
 
 
 def moe_nvfp4_validate(problem, workspace_bytes, arch=None):

@@ -13,6 +13,10 @@
 //     the fp32 scale operand is used).  With scale 1.0 the result is the exact
 //     code value.  byte_sel picks the byte of the source dword.
 //   v_cvt_f32_fp8: one E4M3fn byte -> fp32 (OCP encoding, bias 7, max 448).
+//   v_cvt_scalef32_pk_f16_fp4: the same two codes -> two f16 (exact; with scale
+//     1.0 the code value), used with a packed f16 multiply by the block scale on
+//     the W4A4 tiled path (exact: products of at most 6 significant bits in
+//     f16's normal range); covered by that path's parity tests.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,6 +26,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -78,6 +84,28 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16(uint32_t codes) {
     r.z = __builtin_bit_cast(uint32_t, c);
     r.w = __builtin_bit_cast(uint32_t, d);
     return r;
+}
+
+// Eight E2M1 codes times a block scale (as an f16 pair) -> 8 exact f16 values
+// (4 dwords): a code times an E4M3 scale has at most 6 significant bits and lies
+// in [2^-10, 2688], inside f16's normal range, so the packed f16 products are
+// exact.
+__device__ __forceinline__ u32x4_t dequant8_f16(uint32_t codes, f16x2_t s2) {
+    const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
+    const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+    const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+    const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+    u32x4_t r;
+    r.x = __builtin_bit_cast(uint32_t, a);
+    r.y = __builtin_bit_cast(uint32_t, b);
+    r.z = __builtin_bit_cast(uint32_t, c);
+    r.w = __builtin_bit_cast(uint32_t, d);
+    return r;
+}
+
+// fp32 -> f16 bits (round to nearest even; exact for NVFP4 products).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
 // ---------------------------------------------------------------------------

@@ -45,9 +45,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Path actually used for a problem (AUTO resolved by the expected local load).
 int resolve_path(const moe_nvfp4_problem& p) {
     if (p.path == MOE_NVFP4_PATH_DECODE || p.path == MOE_NVFP4_PATH_PREFILL) return p.path;
-    // expected local pairs per local expert: T * k / E (uniform routing)
+    // expected local pairs per local expert: T * k / E (uniform routing).  The
+    // crossover was measured on the 4096 x 1024 layer: the tiled kernels stay
+    // near-flat in T while weight streaming grows with the rows per expert;
+    // packed W4A4 tiles move 3.5x fewer activation bytes and cross earlier.
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
-    return per_expert <= 16.0 ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
+    const bool packed = p.mode == MOE_NVFP4_W4A4 && moe::pf_packed_ok(p.d_model, p.d_ff);
+    return per_expert <= (packed ? 2.0 : 6.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
 }
 
 struct Plan {
@@ -234,6 +238,14 @@ int moe_nvfp4_validate(const moe_nvfp4_problem* p, size_t workspace_bytes, const
     return ok();
 }
 
+int moe_nvfp4_resolved_path(const moe_nvfp4_problem* p, int32_t* path) {
+    if (!path) return fail(MOE_NVFP4_ERR_INVALID_ARG, "path is NULL");
+    const int st = check_problem(p);
+    if (st) return st;
+    *path = resolve_path(*p);
+    return ok();
+}
+
 int moe_nvfp4_forward(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w,
                       const moe_nvfp4_weights* local, const moe_nvfp4_weights* shared, void* workspace,
                       size_t workspace_bytes, void* out, void* stream) {
@@ -276,10 +288,23 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
         return st;
     if ((st = mark(1))) return st;
     const bool w4a4 = p->mode == MOE_NVFP4_W4A4;
+    const bool tiled = pl.path == MOE_NVFP4_PATH_PREFILL;
+    // W4A4 on the tiled path: the activations travel as NVFP4 codes and scales
+    // when d and F allow it, else as exact f16 values
+    const bool packed = w4a4 && tiled && moe::pf_packed_ok(p->d_model, p->d_ff);
+    uint8_t* hq_codes = at<uint8_t>(workspace, pl.hq);
+    uint8_t* hq_scales = hq_codes + (size_t)p->num_tokens * (p->d_model / 2);
+    uint8_t* act_codes = at<uint8_t>(workspace, pl.act);
+    uint8_t* act_scales = act_codes + (size_t)pl.rows * (p->d_ff / 2);
     if (w4a4) {
-        st = hip_status(moe::launch_fake_quant_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
-                                                   p->d_model, at<uint16_t>(workspace, pl.hq), s),
-                        "activation quantizer launch");
+        if (packed)
+            st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
+                                                     p->d_model, hq_codes, hq_scales, s),
+                            "activation quantizer launch");
+        else
+            st = hip_status(moe::launch_fake_quant_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
+                                                       p->d_model, at<uint16_t>(workspace, pl.hq), tiled, s),
+                            "activation quantizer launch");
         if (st) return st;
     }
     if ((st = mark(2))) return st;
@@ -297,6 +322,11 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     g.shared = to_internal(p->has_shared ? shared : nullptr);
     g.act = at<uint16_t>(workspace, pl.act);
     g.Y = at<uint16_t>(workspace, pl.Y);
+    g.packed = packed ? 1 : 0;
+    g.hq_codes = hq_codes;
+    g.hq_scales = hq_scales;
+    g.act_codes = act_codes;
+    g.act_scales = act_scales;
     const bool dec = pl.path == MOE_NVFP4_PATH_DECODE;
     if ((st = hip_status(dec ? moe::launch_dec_gemm1(g, s) : moe::launch_gemm1(g, pl.path, s), "gemm1 launch")))
         return st;

@@ -46,10 +46,20 @@ struct GemmArgs {
     const int32_t* ntiles;
     int max_tiles;
     const uint16_t* hidden;       // bf16 [T][d]
-    const uint16_t* hq;           // W4A4: hidden NVFP4-quantized, exact dequantized bf16 [T][d]
+    const uint16_t* hq;           // W4A4: hidden NVFP4-quantized, exact dequantized [T][d]
+                                  //   (bf16 on the decode path, f16 on the tiled path)
     ExpertWeights local, shared;
-    uint16_t* act;                // SwiGLU output bf16 [R][F] (W4A4: exact dequantized NVFP4 values)
+    uint16_t* act;                // SwiGLU output [R][F]: bf16; W4A4: exact dequantized NVFP4
+                                  //   values, bf16 (decode path) or f16 (tiled path)
     uint16_t* Y;                  // expert outputs, bf16 [R][d];  R = T*k + T
+    // W4A4 on the tiled path when d and F are multiples of 256 (packed != 0):
+    // activations travel as NVFP4 codes and E4M3 block scales instead of 16-bit
+    // values (in the hq and act regions)
+    int packed;
+    const uint8_t* hq_codes;      // [T][d/2]
+    const uint8_t* hq_scales;     // [T][d/16]
+    uint8_t* act_codes;           // [R][F/2]
+    uint8_t* act_scales;          // [R][F/16]
 };
 
 struct CombineArgs {
@@ -65,7 +75,7 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);
-hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, hipStream_t s);
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, bool f16_out, hipStream_t s);
 hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
@@ -74,6 +84,7 @@ hipError_t launch_prepare_rows(const uint8_t* src, uint8_t* dst, int n, int rows
 hipError_t launch_prepare_global(const float* src, float* dst, int n, bool inverse, hipStream_t s);
 int gemm_bm(int path, int T, int topk, int E);   // rows per tile of the chosen path
 int pf_rows();                                    // rows per tile of the prefill GEMMs
+bool pf_packed_ok(int d, int F);                  // W4A4 packed-activation GEMMs apply
 int dec_rows(int T, int topk, int E);
 hipError_t launch_gemm1(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);

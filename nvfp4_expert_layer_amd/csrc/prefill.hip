@@ -1,30 +1,41 @@
 // Tiled expert GEMMs for many tokens per expert (prefill), gfx950.
 //
 // A tile is 256 pair rows of one expert group (a local expert, or the shared
-// expert over all tokens) x 256 weight rows, K staged 64 at a time (160 KB of
-// LDS, the whole of a CU's):
-//   A: the tile's bf16 activation rows, copied straight from global memory into
-//      a 3-slot LDS ring (global_load_lds_dwordx4, no registers), gathered
-//      through the permutation for GEMM1;
-//   B: the 256 weight rows' NVFP4 codes and E4M3 block scales, decoded ONCE per
-//      workgroup to exact bf16 (code * scale has at most 6 significant bits)
-//      into a 2-slot LDS buffer.
-// Both are [row][64] bf16 with the eight 16-byte chunks of a row XOR-swizzled by
-// (row & 7), so the MFMA operand reads (32 rows x one chunk) hit distinct banks.
-// WAVES = 8 (two per SIMD, the default) or 4 (one per SIMD) waves as 2 (rows) x
-// WAVES/2 (weight rows); a wave owns 128 x (512/WAVES) of the tile as blocks of
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Two waves per SIMD hide each
-// other's LDS waits; one wave per SIMD halves the B operand reads but stalls on
-// every LDS wait (measured slower).  Lane layout of
-// that instruction (checked on the device): lane l holds A[l%32][8(l/32)..+8]
-// and B[8(l/32)..+8][l%32]; accumulator value v sits at row 8(v/4) + 4(l/32) +
-// v%4, column l%32.
+// expert over all tokens) x 256 weight rows, K staged 64 at a time.  Eight
+// waves as 2 (rows) x 4 (weight rows); a wave owns 128 x 64 of the tile as
+// 4 x 2 blocks of 32x32x16 MFMAs with fp32 accumulation.  LDS (155 KB of the
+// CU's 160 KB):
+//   A ring, 4 slots of [256 rows][64] 16-bit activations, copied straight from
+//     global memory (global_load_lds_dwordx4, no registers), gathered through
+//     the permutation for GEMM1; the eight 16-byte chunks of a row are
+//     XOR-swizzled by the row so that a 32-row operand read is conflict-free;
+//   raw ring, 3 slots of the 256 weight rows' NVFP4 codes (32 bytes a row) and
+//     E4M3 block scales (4 bytes a row) for the step, copied the same way.
+// Every wave decodes its own weight operand from the raw ring into registers:
+// code * block scale is exact in 16 bits (at most 6 significant bits).  The
+// weight tile is never written back to LDS, so the LDS carries only the A
+// operand reads and the two rings' fills.
+//
+// K order inside a step: the MFMA sums over its 16 k in any order as long as
+// both operands use the same one.  Lane half h of MFMA kk (0..3) takes the
+// step's k = 32h + 8kk .. +8, so one 16-byte read of a weight row's raw codes
+// (k = 32h .. 32h + 32) gives a lane its codes for all four MFMAs, and the A
+// operand is chunk 4h + kk of the row.
+//
+// Operand type: W4A16 multiplies bf16 activations by bf16-decoded weights.  In
+// W4A4 both operands are NVFP4 products (code * E4M3 scale), exact in f16 as in
+// bf16, so the activations arrive as f16 and the weights decode with packed f16
+// multiplies (v_mfma_f32_32x32x16_f16); the arithmetic is the same.
+//
+// Lane layout of v_mfma_f32_32x32x16_{bf16,f16} (checked on the device): lane
+// l holds A[l%32][8(l/32)..+8] and B[8(l/32)..+8][l%32]; accumulator value v
+// sits at row 8(v/4) + 4(l/32) + v%4, column l%32.
 //
 // GEMM1 (KIND 1): the 256 weight rows are 128 gate rows [n, n+128) and the
-// matching up rows [F+n, F+n+128); a wave's column blocks are gate columns and
-// the same up columns, so the SwiGLU a = silu(g13*gate) * (g13*up) is formed
-// in registers; W4A4 quantize-dequantizes a per 16 columns (16 lanes).  Stored
-// bf16.
+// matching up rows [F+n, F+n+128); a wave's two column blocks are gate columns
+// and the same up columns, so the SwiGLU a = silu(g13*gate) * (g13*up) is formed
+// in registers; W4A4 quantize-dequantizes a per 16 columns.  Stored bf16
+// (W4A16) or f16 (W4A4, exact).
 // GEMM2 (KIND 2): Y = g2 * acc, bf16 rows (through LDS, 16-byte stores).
 //
 // Workgroups are mapped so that each of the 8 XCDs (hardware workgroup b runs on
@@ -43,34 +54,47 @@ namespace moe {
 constexpr int kPM = 256;                       // tile rows
 constexpr int kPN = 256;                       // tile weight rows
 constexpr int kPK = 64;                        // K per stage
+constexpr int kPWaves = 8;
 constexpr int kPA = kPM * kPK * 2;             // bytes of one A stage (32 KB)
-constexpr int kPB = kPN * kPK * 2;             // bytes of one decoded B stage (32 KB)
+constexpr int kPASlots = 4;
 constexpr int kPRawC = kPN * (kPK / 2);        // raw codes of one step (8 KB: 32 B per weight row)
 constexpr int kPRaw = kPRawC + kPN * 4;        // + raw scales (1 KB: 4 B per weight row)
-constexpr int kPOffB = 2 * kPA;                // LDS map: A[2] | B[2] | raw[3]
-constexpr int kPOffR = kPOffB + 2 * kPB;
-constexpr int kPLds = kPOffR + 3 * kPRaw;      // 155 KB of the CU's 160 KB
+constexpr int kPRSlots = 3;
+constexpr int kPOffR = kPASlots * kPA;         // LDS map: A[4] | raw[3]
+constexpr int kPLds = kPOffR + kPRSlots * kPRaw;   // 155 KB
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
 
-// Byte offset of 16-byte chunk c of row r in a swizzled [rows][64 bf16] tile.
-// Any 8 consecutive rows (aligned) put a given chunk in 8 different 16-byte
-// slots, and rows r, r + 8 differ again in the slot's low bit, so a 32-row
-// operand read is free of bank conflicts whether the LDS serves 8 or 16 lanes of
-// a 16-byte access per cycle.
+// Byte offset of 16-byte chunk c of row r in a swizzled [rows][64 x 16-bit]
+// tile.  Any 8 consecutive rows (aligned) put a given chunk in 8 different
+// 16-byte slots, and rows r, r + 8 differ again in the slot's low bit, so a
+// 32-row operand read is free of bank conflicts whether the LDS serves 8 or 16
+// lanes of a 16-byte access per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
 
-template <int KIND, int MODE, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
-    constexpr int WN = WAVES / 2;                  // waves along the weight rows
-    constexpr int NJ = kPN / WN / 32;              // 32-column blocks per wave (2 or 4)
-    constexpr int NA = 32 / WAVES;                 // A loads (1 KB) per wave per step
-    constexpr int NC = 8 / WAVES;                  // raw code loads (1 KB) per wave per step
-    constexpr int SL = 256 / WAVES;                // raw scale rows per wave (lanes)
-    constexpr int NLOAD = NA + NC + 1;             // direct loads per wave per step
-    constexpr int NRAW = NC + 1;                   // of which raw (issued last)
+// Raw code rows: the two 16-byte halves of weight row r are stored swapped when
+// rawf(r) = 1, so that 32 lanes reading one half of 32 consecutive rows
+// (32-byte stride) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int rawf(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+template <int MODE>
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+    if constexpr (MODE == 1)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int KIND, int MODE>
+__global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
+    constexpr int WN = kPWaves / 2;                // waves along the weight rows
+    constexpr int NJ = kPN / WN / 32;              // 32-column blocks per wave (2)
+    constexpr int NA = 32 / kPWaves;               // A loads (1 KB) per wave per step (4)
+    static_assert(NJ == 2 && NA == 4, "tile shape");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int d = a.d, F = a.F;
     const int NT = KIND == 1 ? (2 * F) / kPN : (d + kPN - 1) / kPN;
@@ -110,22 +134,20 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
                   (((lane & 7) ^ (lane >> 3) ^ (q & 1)) << 3);
     }
 
-    // ---- raw weight sources (copied to LDS as they are, decoded from there) ----
-    // codes: load q of wave w, lane i -> weight row r = 32 (NC w + q) + i/2, bytes
-    // 16 (i%2) .. +16 of its 32 code bytes per step, landing at raw + 32 r + 16 (i%2)
-    // = raw + 1024 (NC w + q) + 16 i;  scales: lane i < SL -> row SL w + i, its 4
-    // scale bytes per step at raw + 8 KB + 4 r = raw + 8 KB + 4 SL w + 4 i.
+    // ---- raw weight sources ----
+    // codes: wave w, lane i -> weight row r = 32 w + i/2; it copies the half
+    // (i%2) ^ rawf(r) of the row's 32 code bytes of the step to raw + 32 r + 16 (i%2)
+    // = raw + 1024 w + 16 i.  scales: lane i < 32 -> row 32 w + i, its 4 scale
+    // bytes of the step at raw + 8 KB + 4 r = raw + 8 KB + 128 w + 4 i.
     auto weight_row = [&](int r) {
         if (KIND == 1) return (r < 128 ? 0 : F - 128) + nt * 128 + r;
         return min(nt * kPN + r, d - 1);                 // columns past d: any valid row
     };
     const uint8_t* wcodes = KIND == 1 ? W.w13 + ex * (size_t)(2 * F) * (d / 2) : W.w2 + ex * (size_t)d * (F / 2);
     const uint8_t* wscales = KIND == 1 ? W.w13_s + ex * (size_t)(2 * F) * (d / 16) : W.w2_s + ex * (size_t)d * (F / 16);
-    const uint8_t* csrc[NC];
-#pragma unroll
-    for (int q = 0; q < NC; ++q)
-        csrc[q] = wcodes + (size_t)weight_row((wave * NC + q) * 32 + (lane >> 1)) * (K / 2) + (lane & 1) * 16;
-    const uint8_t* ssrc = wscales + (size_t)weight_row(wave * SL + (lane & (SL - 1))) * (K / 16);
+    const int crow = wave * 32 + (lane >> 1);
+    const uint8_t* csrc = wcodes + (size_t)weight_row(crow) * (K / 2) + ((lane & 1) ^ rawf(crow)) * 16;
+    const uint8_t* ssrc = wscales + (size_t)weight_row(wave * 32 + (lane & 31)) * (K / 16);
     const float gscale = KIND == 1 ? W.g13[ex] : W.g2[ex];
 
     // valid 32-row blocks of this wave (rows past re are padding)
@@ -133,49 +155,22 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
     const bool colv = KIND == 1 || nt * kPN + wn * (32 * NJ) < d;
     const int nk = K / kPK;
 
-    // Every wave issues exactly NLOAD direct loads per step, in this order: NA
-    // A loads, then NC raw code loads and one raw scale load (lanes < SL).
-    auto issue_raw = [&](int ks_r, int rslot) {
-        uint8_t* rbase = smem + kPOffR + rslot * kPRaw;
-#pragma unroll
-        for (int q = 0; q < NC; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)(csrc[q] + ks_r * (kPK / 2)),
-                                             (lds_void_t*)(rbase + (wave * NC + q) * 1024), 16, 0, 0);
-        if (SL == 64 || lane < SL)
-            __builtin_amdgcn_global_load_lds((const void*)(ssrc + ks_r * (kPK / 16)),
-                                             (lds_void_t*)(rbase + kPRawC + wave * SL * 4), 4, 0, 0);
+    // Direct loads per wave per step, in this order: one raw code load, one raw
+    // scale load (lanes < 32), then NA A loads.
+    auto issue_raw = [&](int ks, int slot) {
+        uint8_t* rbase = smem + kPOffR + slot * kPRaw;
+        __builtin_amdgcn_global_load_lds((const void*)(csrc + ks * (kPK / 2)), (lds_void_t*)(rbase + wave * 1024),
+                                         16, 0, 0);
+        if (lane < 32)
+            __builtin_amdgcn_global_load_lds((const void*)(ssrc + ks * (kPK / 16)),
+                                             (lds_void_t*)(rbase + kPRawC + wave * 128), 4, 0, 0);
     };
-    auto issue = [&](int ks_a, int aslot, int ks_r, int rslot) {
-        uint8_t* abase = smem + aslot * kPA + wave * NA * 1024;
+    auto issue_a = [&](int ks, int slot) {
+        uint8_t* abase = smem + slot * kPA + wave * NA * 1024;
 #pragma unroll
         for (int q = 0; q < NA; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)(asrc[q] + ks_a * kPK), (lds_void_t*)(abase + q * 1024),
-                                             16, 0, 0);
-        asm volatile("" ::: "memory");               // keep the A loads ahead of the raw loads
-        issue_raw(ks_r, rslot);
-    };
-
-    // decode: thread -> B row bj = tid % 256, chunks CB .. CB + NQ of the row's 8
-    // (8 waves: two threads per row, a K half each; 4 waves: one thread per row);
-    // 16 lanes of a wave write 16 consecutive rows' same chunk: conflict-free
-    constexpr int NQ = WAVES == 8 ? 4 : 8;
-    const int bj = tid & 255, cb = (tid >> 8) * NQ;
-    struct Raw { u32x4_t c[NQ / 4]; uint32_t s; };
-    auto read_raw = [&](int rslot) {
-        const uint8_t* rb0 = smem + kPOffR + rslot * kPRaw;
-        Raw r;
-#pragma unroll
-        for (int h = 0; h < NQ / 4; ++h) r.c[h] = *reinterpret_cast<const u32x4_t*>(rb0 + bj * 32 + cb * 4 + h * 16);
-        r.s = *reinterpret_cast<const uint32_t*>(rb0 + kPRawC + bj * 4);
-        return r;
-    };
-    // chunk q (0..NQ) of this thread: 8 elements, scale byte (cb + q) / 2
-    auto store_b8 = [&](const Raw& r, int q, int bslot) {
-        uint8_t* base = smem + kPOffB + bslot * kPB;
-        const int c = cb + q;
-        const float s = e4m3_to_f32((r.s >> ((c >> 1) * 8)) & 0xFFu);
-        const uint32_t codes = r.c[q >> 2][q & 3];
-        *reinterpret_cast<u32x4_t*>(base + swz(bj, c)) = dequant8_bf16(codes, s);
+            __builtin_amdgcn_global_load_lds((const void*)(asrc[q] + ks * kPK), (lds_void_t*)(abase + q * 1024), 16,
+                                             0, 0);
     };
 
     f32x16_t acc[4][NJ];
@@ -186,84 +181,89 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    // LDS rows of this lane's operands: A rows wm*128 + 32 i; B blocks j < NJ
-    // (GEMM1: gate (NJ/2) 32 wn + 32 j for j < NJ/2, the matching up rows 128
-    // further; GEMM2: 32 NJ wn + 32 j)
+    // operand rows of this lane: A rows wm*128 + 32 i + l%32; weight rows (tile
+    // local) GEMM1: gate 32 wn + l%32 and up 128 + 32 wn + l%32; GEMM2: 64 wn +
+    // 32 j + l%32
     const int arow0 = wm * 128 + (lane & 31);
-    int brow[NJ];
+    const int h = lane >> 5;
+    int roff[NJ], soff[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-        brow[j] = (KIND == 1 ? (j < NJ / 2 ? wn * 16 * NJ + j * 32 : 128 + wn * 16 * NJ + (j - NJ / 2) * 32)
-                             : wn * 32 * NJ + j * 32) +
-                  (lane & 31);
-    const int khalf = lane >> 5;
+    for (int j = 0; j < NJ; ++j) {
+        const int br = (KIND == 1 ? j * 128 + wn * 32 : wn * 64 + j * 32) + (lane & 31);
+        roff[j] = br * 32 + ((h ^ rawf(br)) << 4);
+        soff[j] = kPRawC + br * 4;
+    }
 
-    // Pipeline, step ks (A slot ks % 2, B slot ks % 2, raw slot ks % 3):
-    //   issue A(ks+1) and the raw weights of step ks+3 (three raw slots);
-    //   decode the raw weights of step ks+1 into the other B slot, between the
-    //   MFMAs of step ks;
-    //   end: wait until only this step's NRAW raw loads may be outstanding, so
-    //   A(ks+1) and raw(ks+2) have landed; LDS writes done; workgroup barrier.
+    // Pipeline, step ks (A slot ks % 4, raw slot ks % 3):
+    //   issue raw(ks+2) and A(ks+3) into the slots freed by the last barrier;
+    //   read this step's raw codes and scales, decode each MFMA's weight operand
+    //   in registers just before it, A operands double-buffered in registers;
+    //   end: wait until raw(ks+1) (and everything issued before it, A(ks+1)
+    //   included) has landed: only A(ks+2), raw(ks+2), A(ks+3) may still be in
+    //   flight (NA + 2 + NA = 10 loads); LDS reads done; workgroup barrier.
     // Nothing in the loop loads into registers from global memory, so every wait
     // on the direct loads is this explicit one.  Past the end the loads are
     // clamped to the last step (re-loads of valid data into free slots).
     auto kloop = [&](auto nv_c) {
         constexpr int NV = decltype(nv_c)::value;
-        int r0 = 0;                                      // raw slot of step ks
+        int rs = 0;                                        // raw slot of step ks
         for (int ks = 0; ks < nk; ++ks) {
-            const int cur = ks & 1;
-            const int r1 = r0 == 2 ? 0 : r0 + 1;          // raw slot of ks + 1 (and of ks + 4)
-            issue(min(ks + 1, nk - 1), cur ^ 1, min(ks + 3, nk - 1), r0);
-            const Raw raw = read_raw(r1);
-            const uint8_t* As = smem + cur * kPA;
-            const uint8_t* Bs = smem + kPOffB + cur * kPB;
-            bf16x8_t av[2][4], bv[2][NJ];
-            auto frag = [&](int kk, int f) {
-                const int c = kk * 2 + khalf;
+            const int rs2 = rs == 0 ? 2 : rs - 1;          // (ks + 2) % 3
+            issue_raw(min(ks + 2, nk - 1), rs2);
+            issue_a(min(ks + 3, nk - 1), (ks + 3) & 3);
+            if (NV > 0) {
+                const uint8_t* As = smem + (ks & 3) * kPA;
+                const uint8_t* Rs = smem + kPOffR + rs * kPRaw;
+                u32x4_t rc[NJ];
+                uint32_t sc[NJ];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bv[f][j] = *reinterpret_cast<const bf16x8_t*>(Bs + swz(brow[j], c));
+                for (int j = 0; j < NJ; ++j) {
+                    rc[j] = *reinterpret_cast<const u32x4_t*>(Rs + roff[j]);
+                    sc[j] = *reinterpret_cast<const uint32_t*>(Rs + soff[j]) >> (16 * h);
+                }
+                u32x4_t av[2][4];
+                auto frag = [&](int kk, int f) {
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    av[f][i] = *reinterpret_cast<const bf16x8_t*>(As + swz(arow0 + i * 32, c));
-            };
-            if (NV > 0) frag(0, 0);
+                    for (int i = 0; i < NV; ++i)
+                        av[f][i] = *reinterpret_cast<const u32x4_t*>(As + swz(arow0 + i * 32, 4 * h + kk));
+                };
+                frag(0, 0);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (NV > 0) {
+                for (int kk = 0; kk < 4; ++kk) {
                     if (kk < 3) frag(kk + 1, (kk + 1) & 1);
+                    u32x4_t bv[NJ];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const uint32_t sbyte = (sc[j] >> (8 * (kk >> 1))) & 0xFFu;
+                        if constexpr (MODE == 1) {
+                            const _Float16 s = (_Float16)e4m3_to_f32(sbyte);
+                            bv[j] = dequant8_f16(rc[j][kk], f16x2_t{s, s});
+                        } else {
+                            bv[j] = dequant8_bf16(rc[j][kk], e4m3_to_f32(sbyte));
+                        }
+                    }
 #pragma unroll
                     for (int i = 0; i < NV; ++i)
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk & 1][i], bv[kk & 1][j],
-                                                                                acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<MODE>(av[kk & 1][i], bv[j], acc[i][j]);
                 }
-#pragma unroll
-                for (int q = kk * NQ / 4; q < (kk + 1) * NQ / 4; ++q) store_b8(raw, q, cur ^ 1);
             }
             // Written out because __syncthreads() would also wait for every
             // outstanding load (vmcnt(0)) and drain the pipeline; the memory
             // clobber keeps the compiler from moving LDS accesses across it.
-            if (NRAW == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            r0 = r1;
+            asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            rs = rs == 2 ? 0 : rs + 1;
         }
     };
 
-    // prologue: A(0); raw of steps 0, 1, 2; decode step 0
-    {
-        uint8_t* abase = smem + wave * NA * 1024;
-#pragma unroll
-        for (int q = 0; q < NA; ++q)
-            __builtin_amdgcn_global_load_lds((const void*)asrc[q], (lds_void_t*)(abase + q * 1024), 16, 0, 0);
-        for (int st = 0; st < 3; ++st) issue_raw(min(st, nk - 1), st);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        const Raw raw = read_raw(0);
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) store_b8(raw, q, 0);
-        __syncthreads();
-    }
+    // prologue: A(0), raw(0), A(1), raw(1), A(2) -- the steady-state issue order
+    // (raw(m), A(m+1)) preceded by A(0); then wait as at the end of a step
+    issue_a(0, 0);
+    issue_raw(0, 0);
+    issue_a(min(1, nk - 1), 1);
+    issue_raw(min(1, nk - 1), 1);
+    issue_a(min(2, nk - 1), 2);
+    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
     switch (colv ? nvi : 0) {
         case 4: kloop(std::integral_constant<int, 4>{}); break;
         case 3: kloop(std::integral_constant<int, 3>{}); break;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
         // SwiGLU in registers, then through LDS (fp32 [256][136]: the 4-row offset
         // of the two half-waves is half a bank period) so that each thread owns
         // whole 16-column blocks of a row: the W4A4 block scale is computed once
-        // per block, and the bf16 row pieces leave in 16-byte stores.
+        // per block, and the 16-bit row pieces leave in 16-byte stores.
         constexpr int ES = 136;                           // row stride (floats)
         float* E = reinterpret_cast<float*>(smem);
         __syncthreads();                                  // every wave's direct loads have landed
@@ -287,20 +287,17 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (i >= nvi) break;
+                const int col = wn * 32 + (lane & 31);
 #pragma unroll
-                for (int j = 0; j < NJ / 2; ++j) {
-                    const int col = wn * 16 * NJ + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
-                        E[row * ES + col] = silu_fast(acc[i][j][v] * gscale) * (acc[i][j + NJ / 2][v] * gscale);
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                    E[row * ES + col] = silu_fast(acc[i][0][v] * gscale) * (acc[i][1][v] * gscale);
                 }
             }
         }
         __syncthreads();
         const int nrow = re - rb;
-        for (int blk = tid; blk < kPM * 8; blk += 64 * WAVES) {
+        for (int blk = tid; blk < kPM * 8; blk += 64 * kPWaves) {
             const int row = blk >> 3, cb = (blk & 7) * 16;
             if (row >= nrow) break;                       // rows grow with blk
             float x[16];
@@ -309,6 +306,7 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
                 const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(E + row * ES + cb + q * 4);
                 x[4 * q] = v4[0]; x[4 * q + 1] = v4[1]; x[4 * q + 2] = v4[2]; x[4 * q + 3] = v4[3];
             }
+            uint32_t o[8];
             if (MODE == 1) {
                 float m = 0.f;
 #pragma unroll
@@ -317,19 +315,15 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                     x[e] = sc > 0.0f ? e2m1_value(e2m1_encode(__fdiv_rn(x[e], sc))) * sc : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_bits(x[2 * e]) | (f32_to_f16_bits(x[2 * e + 1]) << 16);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
             }
-            u32x4_t o0, o1;
-            o0.x = f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16);
-            o0.y = f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16);
-            o0.z = f32_to_bf16_rne(x[4]) | (f32_to_bf16_rne(x[5]) << 16);
-            o0.w = f32_to_bf16_rne(x[6]) | (f32_to_bf16_rne(x[7]) << 16);
-            o1.x = f32_to_bf16_rne(x[8]) | (f32_to_bf16_rne(x[9]) << 16);
-            o1.y = f32_to_bf16_rne(x[10]) | (f32_to_bf16_rne(x[11]) << 16);
-            o1.z = f32_to_bf16_rne(x[12]) | (f32_to_bf16_rne(x[13]) << 16);
-            o1.w = f32_to_bf16_rne(x[14]) | (f32_to_bf16_rne(x[15]) << 16);
             uint16_t* dst = a.act + (size_t)(rb + row) * F + nt * 128 + cb;
-            *reinterpret_cast<u32x4_t*>(dst) = o0;
-            *reinterpret_cast<u32x4_t*>(dst + 8) = o1;
+            *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4_t*>(dst + 8) = u32x4_t{o[4], o[5], o[6], o[7]};
         }
         return;
     }
@@ -357,7 +351,7 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
     const int nrow = re - rb, ncol = min(kPN, d - nt * kPN);
-    for (int pc = tid; pc < kPM * (kPN / 8); pc += 64 * WAVES) {
+    for (int pc = tid; pc < kPM * (kPN / 8); pc += 64 * kPWaves) {
         const int row = pc >> 5, c8 = (pc & 31) * 8;
         if (row >= nrow) break;                           // rows grow with pc
         if (c8 < ncol)
@@ -366,13 +360,284 @@ __global__ __launch_bounds__(64 * WAVES) void pf_gemm_kernel(GemmArgs a) {
     }
 }
 
-constexpr int kPWaves = 8;
+// ---------------------------------------------------------------------------
+// W4A4 with the activations as NVFP4 (codes + E4M3 block scales), for d and F
+// multiples of 256.  The same tile, waves and K order as above, but K is staged
+// 256 at a time (a chunk of four 64-k steps) and BOTH operands arrive raw:
+// per chunk and operand, 256 rows x 128 code bytes (one full 128-byte line a
+// row) and 256 rows x 16 scale bytes, 72 KB a slot, two slots.  Every wave
+// decodes its A and B operands in registers (code * scale, exact in f16).
+// Compared with 16-bit activations this moves 3.5x fewer activation bytes and
+// touches 4x fewer cache lines per step, and the LDS carries no decoded tile.
+// ---------------------------------------------------------------------------
+constexpr int kQK = 256;                             // K per chunk
+constexpr int kQCodes = kPM * (kQK / 2);             // 32 KB of codes per operand and chunk
+constexpr int kQScales = kPM * (kQK / 16);           // 4 KB of scales per operand and chunk
+constexpr int kQSlot = 2 * kQCodes + 2 * kQScales;   // A codes | B codes | A scales | B scales
+constexpr int kQLds = 2 * kQSlot;                    // 144 KB
+
+bool pf_packed_ok(int d, int F) { return d % kQK == 0 && F % kQK == 0; }
+
+template <int KIND, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
+    constexpr int WN = WAVES / 2;                  // waves along the weight rows
+    constexpr int NJ = kPN / WN / 32;              // 32-column blocks per wave (2 or 4)
+    constexpr int NQ = 32 / WAVES;                 // code loads per operand, wave and chunk
+    constexpr int SR = 256 / WAVES;                // scale rows per wave (lanes)
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int d = a.d, F = a.F;
+    const int NT = KIND == 1 ? (2 * F) / kPN : d / kPN;
+    const int total = *a.ntiles * NT;
+    const int b = blockIdx.x, per = (total + 7) >> 3;
+    if ((b >> 3) >= per) return;
+    const int logical = (b & 7) * per + (b >> 3);
+    if (logical >= total) return;
+    const int tile = logical / NT, nt = logical - tile * NT;
+    const int4 tl = a.tiles[tile];
+    const int grp = tl.x, rb = tl.y, re = tl.z;
+    const bool shared = grp == a.L;
+    const ExpertWeights& W = shared ? a.shared : a.local;
+    const size_t ex = shared ? 0 : (size_t)grp;
+    const int K = KIND == 1 ? d : F;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+
+    // activation row of tile row r (padding rows read the tile's first row)
+    auto arow = [&](int r) {
+        int gr = rb + r;
+        if (gr >= re) gr = rb;
+        if (KIND == 2) return gr;
+        return shared ? gr - a.T * a.topk : a.perm[gr] / a.topk;
+    };
+    auto weight_row = [&](int r) {
+        if (KIND == 1) return (r < 128 ? 0 : F - 128) + nt * 128 + r;
+        return nt * kPN + r;
+    };
+    const uint8_t* acodes = KIND == 1 ? a.hq_codes : a.act_codes;
+    const uint8_t* ascales = KIND == 1 ? a.hq_scales : a.act_scales;
+    const uint8_t* wcodes = KIND == 1 ? W.w13 + ex * (size_t)(2 * F) * (d / 2) : W.w2 + ex * (size_t)d * (F / 2);
+    const uint8_t* wscales = KIND == 1 ? W.w13_s + ex * (size_t)(2 * F) * (d / 16) : W.w2_s + ex * (size_t)d * (F / 16);
+
+    // code loads: load q (0..3) of wave w fills rows 8 (4w + q) .. +8 of an
+    // operand's [256][128 B] chunk tile (1 KB, lane i at byte 16 i): lane i ->
+    // row r = 8 (4w + q) + i/8, 16-byte slot i%8, which holds unit
+    // (i & 7) ^ (i >> 3) ^ (q & 1) of the row's chunk (the swz layout)
+    const uint8_t* acs[NQ];
+    const uint8_t* bcs[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int r = (wave * NQ + q) * 8 + (lane >> 3);
+        const int u = (lane & 7) ^ (lane >> 3) ^ (q & 1);
+        acs[q] = acodes + (size_t)arow(r) * (K / 2) + u * 16;
+        bcs[q] = wcodes + (size_t)weight_row(r) * (K / 2) + u * 16;
+    }
+    // scale loads (lanes < SR): row SR w + i, its 16 scale bytes of the chunk at
+    // 16 (SR w + i)
+    const int sr = wave * SR + (lane & (SR - 1));
+    const uint8_t* ass = ascales + (size_t)arow(sr) * (K / 16);
+    const uint8_t* bss = wscales + (size_t)weight_row(sr) * (K / 16);
+    const float gscale = KIND == 1 ? W.g13[ex] : W.g2[ex];
+
+    const int nvi = max(0, min(4, (re - rb - wm * 128 + 31) >> 5));
+    const int nc = K / kQK;
+
+    auto issue = [&](int c, int slot) {
+        uint8_t* base = smem + slot * kQSlot;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(acs[q] + c * (kQK / 2)),
+                                             (lds_void_t*)(base + (wave * NQ + q) * 1024), 16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(bcs[q] + c * (kQK / 2)),
+                                             (lds_void_t*)(base + kQCodes + (wave * NQ + q) * 1024), 16, 0, 0);
+        if (SR == 64 || lane < SR) {
+            __builtin_amdgcn_global_load_lds((const void*)(ass + c * (kQK / 16)),
+                                             (lds_void_t*)(base + 2 * kQCodes + wave * SR * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(bss + c * (kQK / 16)),
+                                             (lds_void_t*)(base + 2 * kQCodes + kQScales + wave * SR * 16), 16, 0,
+                                             0);
+        }
+    };
+
+    f32x16_t acc[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int h = lane >> 5;
+    int brow[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        brow[j] = (KIND == 1 ? (j < NJ / 2 ? wn * 16 * NJ + j * 32 : 128 + wn * 16 * NJ + (j - NJ / 2) * 32)
+                             : wn * 32 * NJ + j * 32) +
+                  (lane & 31);
+    const int arow0 = wm * 128 + (lane & 31);
+
+    // one step (64 k) of a chunk: lane half h of MFMA kk takes k = 32h + 8kk ..
+    // +8 of the step: dword kk of the row's 16-byte code unit 2s + h, scale byte
+    // 2h + kk/2 of the step's 4
+    auto step = [&](auto nv_c, const uint8_t* S, int s) {
+        constexpr int NV = decltype(nv_c)::value;
+        u32x4_t ac[4], bc[NJ];
+        uint32_t as[4], bs[NJ];
+        static_assert(NJ <= 4, "operand blocks");
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int r = arow0 + i * 32;
+            ac[i] = *reinterpret_cast<const u32x4_t*>(S + swz(r, 2 * s + h));
+            as[i] = *reinterpret_cast<const uint32_t*>(S + 2 * kQCodes + r * 16 + s * 4) >> (16 * h);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            bc[j] = *reinterpret_cast<const u32x4_t*>(S + kQCodes + swz(brow[j], 2 * s + h));
+            bs[j] = *reinterpret_cast<const uint32_t*>(S + 2 * kQCodes + kQScales + brow[j] * 16 + s * 4) >> (16 * h);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4_t av[4], bv[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const _Float16 sc = (_Float16)e4m3_to_f32((bs[j] >> (8 * (kk >> 1))) & 0xFFu);
+                bv[j] = dequant8_f16(bc[j][kk], f16x2_t{sc, sc});
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const _Float16 sc = (_Float16)e4m3_to_f32((as[i] >> (8 * (kk >> 1))) & 0xFFu);
+                av[i] = dequant8_f16(ac[i][kk], f16x2_t{sc, sc});
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<1>(av[i], bv[j], acc[i][j]);
+        }
+    };
+
+    // Pipeline: chunk c+1 is loaded into the other slot while chunk c is
+    // multiplied; at the end of a chunk every wave waits for its own loads and
+    // the workgroup meets at a barrier (no LDS reads of slot c remain, chunk c+1
+    // has landed).  Nothing loads into registers from global memory in the loop.
+    auto kloop = [&](auto nv_c) {
+        for (int c = 0; c < nc; ++c) {
+            if (c + 1 < nc) issue(c + 1, (c + 1) & 1);
+            const uint8_t* S = smem + (c & 1) * kQSlot;
+            if (decltype(nv_c)::value > 0) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) step(nv_c, S, s);
+            }
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    };
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    switch (nvi) {
+        case 4: kloop(std::integral_constant<int, 4>{}); break;
+        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 2: kloop(std::integral_constant<int, 2>{}); break;
+        case 1: kloop(std::integral_constant<int, 1>{}); break;
+        default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+
+    const int lr = (lane >> 5) * 4;
+    if (KIND == 1) {
+        // SwiGLU, then NVFP4 per 16 columns: packed codes and E4M3 scales of
+        // the act rows (the next GEMM's raw A)
+        constexpr int ES = 136;
+        float* E = reinterpret_cast<float*>(smem);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i >= nvi) break;
+#pragma unroll
+            for (int j = 0; j < NJ / 2; ++j) {
+                const int col = wn * 16 * NJ + j * 32 + (lane & 31);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                    E[row * ES + col] = silu_fast(acc[i][j][v] * gscale) * (acc[i][j + NJ / 2][v] * gscale);
+                }
+            }
+        }
+        __syncthreads();
+        const int nrow = re - rb;
+        for (int blk = tid; blk < kPM * 8; blk += 64 * WAVES) {
+            const int row = blk >> 3, cb = (blk & 7) * 16;
+            if (row >= nrow) break;                       // rows grow with blk
+            float x[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(E + row * ES + cb + q * 4);
+                x[4 * q] = v4[0]; x[4 * q + 1] = v4[1]; x[4 * q + 2] = v4[2]; x[4 * q + 3] = v4[3];
+            }
+            float m = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
+            const uint32_t sbyte = e4m3_encode_nonneg(__fdiv_rn(m, 6.0f));
+            const float sc = e4m3_to_f32(sbyte);
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t cd = sc > 0.0f ? e2m1_encode(__fdiv_rn(x[e], sc)) : 0u;
+                if (e < 8) lo |= cd << (4 * e);
+                else hi |= cd << (4 * (e - 8));
+            }
+            const size_t col = (size_t)nt * 128 + cb;
+            *reinterpret_cast<u32x2_t*>(a.act_codes + (size_t)(rb + row) * (F / 2) + col / 2) = u32x2_t{lo, hi};
+            a.act_scales[(size_t)(rb + row) * (F / 16) + col / 16] = (uint8_t)sbyte;
+        }
+        return;
+    }
+    constexpr int YS = 264;
+    uint16_t* Ys = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i >= nvi) break;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int col = wn * 32 * NJ + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                Ys[row * YS + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * gscale);
+            }
+        }
+    }
+    __syncthreads();
+    const int nrow = re - rb;
+    for (int pc = tid; pc < kPM * (kPN / 8); pc += 64 * WAVES) {
+        const int row = pc >> 5, c8 = (pc & 31) * 8;
+        if (row >= nrow) break;
+        *reinterpret_cast<u32x4_t*>(a.Y + (size_t)(rb + row) * d + nt * kPN + c8) =
+            *reinterpret_cast<const u32x4_t*>(Ys + row * YS + c8);
+    }
+}
+
+constexpr int kQWaves = 8;
+
+template <int KIND>
+static hipError_t launch_pf4(const GemmArgs& a, hipStream_t s) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)pf4_gemm_kernel<KIND, kQWaves>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int NT = KIND == 1 ? (2 * a.F) / kPN : a.d / kPN;
+    const long long n = (long long)a.max_tiles * NT;
+    const long long grid = (n + 7) / 8 * 8;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((pf4_gemm_kernel<KIND, kQWaves>), dim3((unsigned)grid), dim3(64 * kQWaves), kQLds, s, a);
+    return hipGetLastError();
+}
 
 template <int KIND, int MODE>
 static hipError_t launch_pf(const GemmArgs& a, hipStream_t s) {
     static bool attr_set = false;   // per process; the attribute is per function
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pf_gemm_kernel<KIND, MODE, kPWaves>,
+        hipError_t e = hipFuncSetAttribute((const void*)pf_gemm_kernel<KIND, MODE>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
         if (e != hipSuccess) return e;
         attr_set = true;
@@ -381,18 +646,21 @@ static hipError_t launch_pf(const GemmArgs& a, hipStream_t s) {
     const long long n = (long long)a.max_tiles * NT;
     const long long grid = (n + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((pf_gemm_kernel<KIND, MODE, kPWaves>), dim3((unsigned)grid), dim3(64 * kPWaves), kPLds, s, a);
+    hipLaunchKernelGGL((pf_gemm_kernel<KIND, MODE>), dim3((unsigned)grid), dim3(64 * kPWaves), kPLds, s, a);
     return hipGetLastError();
 }
 
 int pf_rows() { return kPM; }
 
+// W4A4 (mode 1): activations and the SwiGLU output are f16 on this path.
 hipError_t launch_gemm1(const GemmArgs& a, int /*path*/, hipStream_t s) {
+    if (a.packed) return launch_pf4<1>(a, s);
     return a.mode == 0 ? launch_pf<1, 0>(a, s) : launch_pf<1, 1>(a, s);
 }
 
 hipError_t launch_gemm2(const GemmArgs& a, int /*path*/, hipStream_t s) {
-    return launch_pf<2, 0>(a, s);
+    if (a.packed) return launch_pf4<2>(a, s);
+    return a.mode == 0 ? launch_pf<2, 0>(a, s) : launch_pf<2, 1>(a, s);
 }
 
 }  // namespace moe

@@ -58,7 +58,10 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 }
 
 // W4A4 activations: NVFP4 quantize-dequantize, one thread per 16-element block,
-// writing the exact dequantized values (code * scale) as bf16.
+// writing the exact dequantized values (code * scale) as bf16, or as f16 (F16)
+// for the tiled GEMMs, which multiply W4A4 operands in f16.  Both are exact: the
+// product has at most 6 significant bits and lies in f16's normal range.
+template <bool F16>
 __global__ __launch_bounds__(256) void fake_quant_act_kernel(const uint16_t* __restrict__ x, long long nblocks,
                                                              uint16_t* __restrict__ out) {
     long long b = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -77,8 +80,10 @@ __global__ __launch_bounds__(256) void fake_quant_act_kernel(const uint16_t* __r
     for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(f[i]));
     uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        o[i] = pack_hi16(nvfp4_fake_quant(f[2 * i], bmax), nvfp4_fake_quant(f[2 * i + 1], bmax));
+    for (int i = 0; i < 8; ++i) {
+        const float lo = nvfp4_fake_quant(f[2 * i], bmax), hi = nvfp4_fake_quant(f[2 * i + 1], bmax);
+        o[i] = F16 ? f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16) : pack_hi16(lo, hi);
+    }
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
     dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
     dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
@@ -143,10 +148,15 @@ hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, 
     return hipGetLastError();
 }
 
-hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, hipStream_t s) {
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, bool f16_out, hipStream_t s) {
     long long nb = (long long)R * (C / kBlock);
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(fake_quant_act_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb, out);
+    if (f16_out)
+        hipLaunchKernelGGL(fake_quant_act_kernel<true>, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
+                           out);
+    else
+        hipLaunchKernelGGL(fake_quant_act_kernel<false>, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
+                           out);
     return hipGetLastError();
 }
 

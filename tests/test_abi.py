@@ -88,3 +88,20 @@ def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
     assert big > small
     p = nv.make_problem(0, 4096, 1024, 320, 8, 0, 160, True, nv.W4A16)
     assert nv.moe_nvfp4_validate(p, nv.moe_nvfp4_workspace_size(p), None) == nv.OK
+
+
+def test_resolved_path_crossover():
+    # expected local pairs per local expert T*k/E: weight streaming up to 6
+    # (W4A16, or W4A4 whose d or F is not a multiple of 256), 2 for packed W4A4
+    def path(T, mode, d=4096, F=1024, force=nv.PATH_AUTO):
+        return nv.moe_nvfp4_resolved_path(nv.make_problem(T, d, F, 320, 8, 0, 160, True, mode, force))
+    assert path(64, nv.W4A16) == nv.PATH_DECODE
+    assert path(240, nv.W4A16) == nv.PATH_DECODE          # 6.0
+    assert path(241, nv.W4A16) == nv.PATH_PREFILL
+    assert path(80, nv.W4A4) == nv.PATH_DECODE            # 2.0
+    assert path(81, nv.W4A4) == nv.PATH_PREFILL
+    assert path(200, nv.W4A4, F=384) == nv.PATH_DECODE    # not packed: threshold 6
+    assert path(8192, nv.W4A16, force=nv.PATH_DECODE) == nv.PATH_DECODE
+    assert path(1, nv.W4A4, force=nv.PATH_PREFILL) == nv.PATH_PREFILL
+    with pytest.raises(nv.MoeNvfp4Error):
+        path(64, nv.W4A16, d=100)
