@@ -148,8 +148,9 @@ def algorithmic(w, counts):
     w13_b = 2 * F * d // 2 + 2 * F * d // 16           # codes + scales per expert
     w2_b = d * F // 2 + d * F // 16
     fp4 = 9 / 16                                       # bytes per element of NVFP4 activations
-    a_in = T * d * (fp4 if w.mode == workloads.W4A4 else 2)
-    act = rows * F * (fp4 if w.mode == workloads.W4A4 else 2)
+    w4a4 = w.mode != workloads.W4A16
+    a_in = T * d * (fp4 if w4a4 else 2)
+    act = rows * F * (fp4 if w4a4 else 2)
     g1_bytes = touched * w13_b + a_in + act
     g2_bytes = touched * w2_b + act + rows * d * 2     # expert outputs are bf16
     layer_bytes = touched * (w13_b + w2_b) + w.E * d * 2 + T * d * 2 + T * d * 2
@@ -165,7 +166,7 @@ def bench_workload(name, steps, warmup, hip):
     local, shared = build_weights(w)
     x = workloads.gen_hidden(w, "cuda")
     gate_w = workloads.gen_gate(w, "cuda").t().contiguous()
-    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode)
+    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode, nv.PATH_AUTO, w.act_global)
     ws = nv.alloc_workspace(p)
     out = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
     for _ in range(warmup):
@@ -240,7 +241,7 @@ def bench_workload(name, steps, warmup, hip):
            "touched_experts": alg["touched"], "local_pairs": alg["P"],
            # the type the GEMMs multiply in: W4A4 on the tiled path multiplies
            # exact NVFP4 products in f16, everything else in bf16
-           "dtype": "f16" if (path == "prefill" and w.mode == workloads.W4A4) else "bf16"}
+           "dtype": "f16" if (path == "prefill" and w.mode != workloads.W4A16) else "bf16"}
     del local, shared, ws
     torch.cuda.empty_cache()
     return w, res
@@ -281,7 +282,7 @@ def cpu_baseline(name, sample_tokens):
     except Exception:
         threads = 1
     t0 = time.perf_counter()
-    moe.forward(x, G, lambda l: q[w.offset + l], q.get(w.E), w.k, w.offset, w.L, w.mode)
+    moe.forward(x, G, lambda l: q[w.offset + l], q.get(w.E), w.k, w.offset, w.L, w.mode, act_global=w.act_global)
     dt = time.perf_counter() - t0
     return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {sample_tokens} of {w.T} tokens of {name} ({len(need)} experts touched); "
@@ -290,9 +291,12 @@ def cpu_baseline(name, sample_tokens):
 
 
 def config_of(w):
-    return {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F, "experts": w.E, "top_k": w.k,
-            "local_expert_offset": w.offset, "num_local_experts": w.L, "shared": int(w.has_shared),
-            "mode": "W4A16" if w.mode == workloads.W4A16 else "W4A4"}
+    c = {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F, "experts": w.E, "top_k": w.k,
+         "local_expert_offset": w.offset, "num_local_experts": w.L, "shared": int(w.has_shared),
+         "mode": {workloads.W4A16: "W4A16", workloads.W4A4: "W4A4", workloads.W4A4_STATIC: "W4A4 static"}[w.mode]}
+    if w.mode == workloads.W4A4_STATIC:
+        c["act_global"] = list(w.act_global)
+    return c
 
 
 def main():

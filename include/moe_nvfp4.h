@@ -25,7 +25,7 @@
  *   ids      = the top_k experts by logit, descending (equal logits: lower id)
  *   w_j      = softmax over the top_k selected logits (= full softmax renormalised)
  *   keep pair (t, j) iff 0 <= ids_j - local_expert_offset < num_local_experts
- *   h_t      = x_t (W4A16)  or  NVFP4-quantize-dequantize(x_t) (W4A4)
+ *   h_t      = x_t (W4A16)  or  NVFP4-quantize-dequantize(x_t) (W4A4, static W4A4)
  *   expert MLP:  u = W13 h (2*d_ff outputs), a = silu(u[0:F]) * u[F:2F],
  *                (W4A4: a = NVFP4-quantize-dequantize(a)),  y = W2 a
  *   out_t    = sum over kept pairs of w_j * y  +  has_shared * y_shared(h_t)
@@ -39,6 +39,12 @@
  * weight decodes as  code * e4m3(scale) * global  (global is a multiplier).
  * W4A4 activations use the same element/scale format with no global scale:
  * scale = E4M3_rne_saturating(block_amax / 6), code = E2M1_rne_saturating(x / scale).
+ * Static W4A4 (the page's third fused-MoE backend variant, "static" NVFP4 W4A4:
+ * a calibrated activation scale fixed ahead of time) gives each of the two
+ * quantization points a per-layer fp32 activation global g_a (act_global13 for
+ * h, act_global2 for a), applied like a weight's global:
+ * scale = E4M3(block_amax / (6 g_a)), code = E2M1(x / (scale g_a)), value =
+ * code * scale * g_a; blocks beyond 6 * 448 * g_a saturate.
  *
  * Numerics: code * scale is exact in bf16 (and in f16); the GEMMs run on bf16
  * MFMA (W4A16) or f16 MFMA on the tiled path in W4A4, where both operands are
@@ -74,7 +80,8 @@ extern "C" {
 
 typedef enum {
     MOE_NVFP4_W4A16 = 0,   /* NVFP4 weights, bf16 activations                     */
-    MOE_NVFP4_W4A4  = 1    /* NVFP4 weights, activations NVFP4-quantized online   */
+    MOE_NVFP4_W4A4  = 1,   /* NVFP4 weights, activations NVFP4-quantized online   */
+    MOE_NVFP4_W4A4_STATIC = 2  /* as W4A4, with calibrated activation globals      */
 } moe_nvfp4_mode;
 
 typedef enum {
@@ -109,6 +116,9 @@ typedef struct {
     int32_t has_shared;           /* 1: this call adds the shared expert (weight 1)      */
     int32_t mode;                 /* moe_nvfp4_mode                                      */
     int32_t path;                 /* moe_nvfp4_path                                      */
+    float act_global13;           /* static W4A4: activation global of h (GEMM1 input);  */
+    float act_global2;            /*   of a (GEMM2 input); finite, 2^-100..2^100.        */
+                                  /*   Ignored in the other modes.                       */
 } moe_nvfp4_problem;
 
 /* NVFP4 weights of n experts (n = num_local_experts, or 1 for the shared
@@ -188,6 +198,14 @@ int moe_nvfp4_quantize_weights(const void *w, int32_t n, int32_t R, int32_t C, u
  *   x bf16 [R][C] (C multiple of 16) -> codes u8 [R][C/2], scales u8 [R][C/16]  */
 int moe_nvfp4_quantize_activations(const void *x, int32_t R, int32_t C, uint8_t *codes,
                                    uint8_t *scales, void *stream);
+
+/* Static W4A4 activation quantizer alone, with the calibrated global g (finite,
+ * 2^-100..2^100; g = 1 gives moe_nvfp4_quantize_activations):
+ *   scale = E4M3_rne_sat(block_amax / (6 g)), code = E2M1_rne_sat(x / (scale g)),
+ *   fp32 products and correctly rounded divisions; a block whose scale is 0
+ *   gets zero codes.  Shapes as above. */
+int moe_nvfp4_quantize_activations_static(const void *x, int32_t R, int32_t C, float g, uint8_t *codes,
+                                          uint8_t *scales, void *stream);
 
 /* Checkpoint preparation (the page "Serving Solar Open 2 on DGX Spark", section
  * "b12x 버전이 실제 NVFP4 체크포인트를 읽어들이도록 만들기": pre-quantized NVFP4

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
 
 W4A16 = 0
 W4A4 = 1
+W4A4_STATIC = 2
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 
 OK = 0
@@ -36,7 +37,8 @@ class MoeNvfp4Error(RuntimeError):
 class moe_nvfp4_problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "d_model", "d_ff", "num_experts", "top_k", "local_expert_offset",
-        "num_local_experts", "has_shared", "mode", "path")]
+        "num_local_experts", "has_shared", "mode", "path")] + [
+        ("act_global13", ctypes.c_float), ("act_global2", ctypes.c_float)]
 
 
 class moe_nvfp4_weights(ctypes.Structure):
@@ -78,13 +80,14 @@ def lib():
         L.moe_nvfp4_route.argtypes = [P(moe_nvfp4_problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_nvfp4_quantize_weights.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.moe_nvfp4_quantize_activations.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_nvfp4_quantize_activations_static.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp, vp]
         L.moe_nvfp4_prepare.argtypes = [P(moe_nvfp4_checkpoint), i32, i32, P(moe_nvfp4_weights), vp]
         L.moe_nvfp4_strerror.argtypes = [ctypes.c_int]
         L.moe_nvfp4_strerror.restype = ctypes.c_char_p
         L.moe_nvfp4_last_error.argtypes = []
         L.moe_nvfp4_last_error.restype = ctypes.c_char_p
         for f in ("workspace_size", "validate", "forward", "forward_timed", "route", "quantize_weights",
-                  "quantize_activations", "prepare"):
+                  "quantize_activations", "quantize_activations_static", "prepare", "resolved_path"):
             getattr(L, "moe_nvfp4_" + f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -111,8 +114,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_problem(T, d, F, E, k, offset, L, has_shared, mode, path=PATH_AUTO):
-    return moe_nvfp4_problem(T, d, F, E, k, offset, L, int(bool(has_shared)), mode, path)
+def make_problem(T, d, F, E, k, offset, L, has_shared, mode, path=PATH_AUTO, act_global=(1.0, 1.0)):
+    """act_global: the static W4A4 activation globals of the GEMM1 and GEMM2
+    inputs (ignored in the other modes)."""
+    return moe_nvfp4_problem(T, d, F, E, k, offset, L, int(bool(has_shared)), mode, path,
+                             float(act_global[0]), float(act_global[1]))
 
 
 @dataclass
@@ -234,6 +240,14 @@ def moe_nvfp4_quantize_activations(x, codes, scales, stream=None):
     """x bf16 [R, C] -> codes uint8 [R, C/2], scales uint8 [R, C/16]."""
     R, C = x.shape
     _check(lib().moe_nvfp4_quantize_activations(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_nvfp4_quantize_activations_static(x, g, codes, scales, stream=None):
+    """Static W4A4 rule with activation global g: x bf16 [R, C] -> codes uint8
+    [R, C/2], scales uint8 [R, C/16]."""
+    R, C = x.shape
+    _check(lib().moe_nvfp4_quantize_activations_static(_ptr(x), R, C, float(g), _ptr(codes), _ptr(scales),
+                                                       _stream(stream)))
 
 
 def quantize_experts(w13, w2, out=None, start=0):

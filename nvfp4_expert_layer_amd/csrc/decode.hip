@@ -343,7 +343,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
     const int wrow = (is_up ? F : 0) + col0 + n;
     const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2)};
     const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16)};
-    const float g13 = W.g13[tl.ex];
+    const float g13 = W.g13[tl.ex] * a.a1g;          // weight global x activation global
     auto epi = [&](int j, const f32x4_t (&acc)[TGM][1]) {
         const int col = col0 + 32 * j + n;
         float v[TGM];
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
                     m = fmaxf(m, __shfl_xor(m, 2, 64));
                     m = fmaxf(m, __shfl_xor(m, 4, 64));
                     m = fmaxf(m, __shfl_xor(m, 8, 64));
-                    av = nvfp4_fake_quant(av, m);
+                    av = nvfp4_fake_quant(av, m, a.a2g);
                 }
                 const int r = tl.rb + tg * 4 + g;
                 if (r < tl.re) a.act[(size_t)r * F + col] = (uint16_t)f32_to_bf16_rne(av);
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
     const uint8_t* const codes[1] = {w2 + (size_t)(cbase + n) * (F / 2)};
     const uint8_t* const scales[1] = {w2s + (size_t)(cbase + n) * (F / 16)};
     const size_t cstride = (size_t)(16 * kDecWaves) * (F / 2), sstride = (size_t)(16 * kDecWaves) * (F / 16);
-    const float g2 = W.g2[tl.ex];
+    const float g2 = W.g2[tl.ex] * a.a2g;            // weight global x activation global
     auto epi = [&](int j, const f32x4_t (&acc)[TGM][1]) {
         const int col = cbase + j * (16 * kDecWaves) + n;
 #pragma unroll

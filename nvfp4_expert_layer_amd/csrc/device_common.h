@@ -164,11 +164,22 @@ __device__ __forceinline__ float e2m1_value(uint32_t code) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code & 0xFu, 1.0f, 0)[0];
 }
 
-// NVFP4 quantize-dequantize of one value given its block's amax (W4A4 rule:
-// scale = E4M3(amax / 6), code = E2M1(x / scale)); returns code * scale exactly.
-__device__ __forceinline__ float nvfp4_fake_quant(float x, float block_amax) {
-    const float s = e4m3_to_f32(e4m3_encode_nonneg(__fdiv_rn(block_amax, 6.0f)));
-    return s > 0.0f ? e2m1_value(e2m1_encode(__fdiv_rn(x, s))) * s : 0.0f;
+// NVFP4 activation block step with an activation global scale g (g = 1: the
+// dynamic rule, scale = E4M3(amax / 6), code = E2M1(x / scale); static: the
+// calibrated g, scale = E4M3(amax / (6 g)), code = E2M1(x / (scale g)), fp32
+// products and correctly rounded divisions, as for weights).
+__device__ __forceinline__ uint32_t nvfp4_act_scale(float block_amax, float g) {
+    return e4m3_encode_nonneg(__fdiv_rn(block_amax, 6.0f * g));
+}
+__device__ __forceinline__ uint32_t nvfp4_act_code(float x, float s, float g) {
+    const float sg = s * g;
+    return sg > 0.0f ? e2m1_encode(__fdiv_rn(x, sg)) : 0u;
+}
+// Quantize-dequantize of one value: returns code * scale exactly (the global g
+// is applied after the GEMM's accumulation).
+__device__ __forceinline__ float nvfp4_fake_quant(float x, float block_amax, float g) {
+    const float s = e4m3_to_f32(nvfp4_act_scale(block_amax, g));
+    return e2m1_value(nvfp4_act_code(x, s, g)) * s;
 }
 
 // Wave-wide reductions (wave64).

@@ -42,6 +42,13 @@ int ok() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// an activation global scale the fp32 quantizer arithmetic handles without
+// overflow or underflow (6 g and 448 g stay finite and normal)
+bool global_ok(float g) { return g >= 0x1p-100f && g <= 0x1p100f; }
+
+// W4A4 in either form (the kernels see mode 1 and the activation globals)
+bool is_w4a4(int mode) { return mode == MOE_NVFP4_W4A4 || mode == MOE_NVFP4_W4A4_STATIC; }
+
 // Path actually used for a problem (AUTO resolved by the expected local load).
 int resolve_path(const moe_nvfp4_problem& p) {
     if (p.path == MOE_NVFP4_PATH_DECODE || p.path == MOE_NVFP4_PATH_PREFILL) return p.path;
@@ -50,7 +57,7 @@ int resolve_path(const moe_nvfp4_problem& p) {
     // near-flat in T while weight streaming grows with the rows per expert;
     // packed W4A4 tiles move 3.5x fewer activation bytes and cross earlier.
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
-    const bool packed = p.mode == MOE_NVFP4_W4A4 && moe::pf_packed_ok(p.d_model, p.d_ff);
+    const bool packed = is_w4a4(p.mode) && moe::pf_packed_ok(p.d_model, p.d_ff);
     return per_expert <= (packed ? 2.0 : 6.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
 }
 
@@ -64,8 +71,10 @@ struct Plan {
 int check_problem(const moe_nvfp4_problem* p) {
     if (!p) return fail(MOE_NVFP4_ERR_INVALID_ARG, "problem is NULL");
     if (p->num_tokens < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "num_tokens < 0");
-    if (p->mode != MOE_NVFP4_W4A16 && p->mode != MOE_NVFP4_W4A4)
+    if (p->mode != MOE_NVFP4_W4A16 && p->mode != MOE_NVFP4_W4A4 && p->mode != MOE_NVFP4_W4A4_STATIC)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown mode %d", p->mode);
+    if (p->mode == MOE_NVFP4_W4A4_STATIC && (!global_ok(p->act_global13) || !global_ok(p->act_global2)))
+        return fail(MOE_NVFP4_ERR_INVALID_ARG, "static W4A4 activation globals must be finite, in 2^-100..2^100");
     if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_PREFILL)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown path %d", p->path);
     if (p->has_shared != 0 && p->has_shared != 1)
@@ -115,7 +124,7 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.ntiles = take(4);
     pl.perm = take(T * k * 4);
     pl.inv = take(T * k * 4);
-    const bool w4a4 = p.mode == MOE_NVFP4_W4A4;
+    const bool w4a4 = is_w4a4(p.mode);
     pl.hq = take(w4a4 ? T * d * 2 : 0);
     pl.act = take(pl.rows * F * 2);
     pl.Y = take(pl.rows * d * 2);
@@ -287,7 +296,9 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     if ((st = run_route(*p, pl, hidden, gate_w, workspace, s, nullptr, nullptr, nullptr, nullptr, nullptr)))
         return st;
     if ((st = mark(1))) return st;
-    const bool w4a4 = p->mode == MOE_NVFP4_W4A4;
+    const bool w4a4 = is_w4a4(p->mode);
+    const bool stat = p->mode == MOE_NVFP4_W4A4_STATIC;
+    const float a1g = stat ? p->act_global13 : 1.0f, a2g = stat ? p->act_global2 : 1.0f;
     const bool tiled = pl.path == MOE_NVFP4_PATH_PREFILL;
     // W4A4 on the tiled path: the activations travel as NVFP4 codes and scales
     // when d and F allow it, else as exact f16 values
@@ -299,18 +310,20 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     if (w4a4) {
         if (packed)
             st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
-                                                     p->d_model, hq_codes, hq_scales, s),
+                                                     p->d_model, a1g, hq_codes, hq_scales, s),
                             "activation quantizer launch");
         else
             st = hip_status(moe::launch_fake_quant_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
-                                                       p->d_model, at<uint16_t>(workspace, pl.hq), tiled, s),
+                                                       p->d_model, a1g, at<uint16_t>(workspace, pl.hq), tiled, s),
                             "activation quantizer launch");
         if (st) return st;
     }
     if ((st = mark(2))) return st;
     moe::GemmArgs g{};
     g.T = p->num_tokens; g.d = p->d_model; g.F = p->d_ff; g.topk = p->top_k; g.L = p->num_local_experts;
-    g.mode = p->mode;
+    g.mode = w4a4 ? 1 : 0;
+    g.a1g = a1g;
+    g.a2g = a2g;
     g.E = p->num_experts;
     g.perm = at<int32_t>(workspace, pl.perm);
     g.tiles = at<int4>(workspace, pl.tiles);
@@ -399,12 +412,18 @@ int moe_nvfp4_quantize_weights(const void* w, int32_t n, int32_t R, int32_t C, u
 
 int moe_nvfp4_quantize_activations(const void* x, int32_t R, int32_t C, uint8_t* codes, uint8_t* scales,
                                    void* stream) {
+    return moe_nvfp4_quantize_activations_static(x, R, C, 1.0f, codes, scales, stream);
+}
+
+int moe_nvfp4_quantize_activations_static(const void* x, int32_t R, int32_t C, float g, uint8_t* codes,
+                                          uint8_t* scales, void* stream) {
     if (!x || !codes || !scales) return fail(MOE_NVFP4_ERR_INVALID_ARG, "NULL pointer");
+    if (!global_ok(g)) return fail(MOE_NVFP4_ERR_INVALID_ARG, "global %g outside 2^-100..2^100", (double)g);
     if (R < 0 || C < 0) return fail(MOE_NVFP4_ERR_INVALID_ARG, "negative size");
     if (C % 16) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "C %d is not a multiple of 16", C);
     int dev, st;
     if ((st = current_arch_ok(&dev))) return st;
-    st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(x), R, C, codes, scales,
+    st = hip_status(moe::launch_quantize_act(static_cast<const uint16_t*>(x), R, C, g, codes, scales,
                                              static_cast<hipStream_t>(stream)),
                     "activation quantizer launch");
     return st ? st : ok();

@@ -41,6 +41,8 @@ struct PermArgs {
 
 struct GemmArgs {
     int T, d, F, topk, L, mode, E;
+    float a1g, a2g;               // activation global scales of the GEMM1 / GEMM2 inputs
+                                  //   (1 unless static W4A4); GEMM inputs hold code * scale
     const int32_t* perm;          // [T*k]
     const int4* tiles;            // (group, row_begin, row_end, -)
     const int32_t* ntiles;
@@ -73,9 +75,10 @@ struct CombineArgs {
 int router_ksplit(int T, int E, int d);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
-hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, uint8_t* scales,
+hipError_t launch_quantize_act(const uint16_t* x, int R, int C, float g, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);
-hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, bool f16_out, hipStream_t s);
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, float g, uint16_t* out, bool f16_out,
+                                 hipStream_t s);
 hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8_t* codes,
                                    uint8_t* scales, float* global, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);

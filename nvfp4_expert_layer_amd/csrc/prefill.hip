@@ -148,7 +148,7 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
     const int crow = wave * 32 + (lane >> 1);
     const uint8_t* csrc = wcodes + (size_t)weight_row(crow) * (K / 2) + ((lane & 1) ^ rawf(crow)) * 16;
     const uint8_t* ssrc = wscales + (size_t)weight_row(wave * 32 + (lane & 31)) * (K / 16);
-    const float gscale = KIND == 1 ? W.g13[ex] : W.g2[ex];
+    const float gscale = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;   // weight x activation globals
 
     // valid 32-row blocks of this wave (rows past re are padding)
     const int nvi = max(0, min(4, (re - rb - wm * 128 + 31) >> 5));
@@ -311,10 +311,9 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
                 float m = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
-                const float sc = e4m3_to_f32(e4m3_encode_nonneg(__fdiv_rn(m, 6.0f)));
+                const float sc = e4m3_to_f32(nvfp4_act_scale(m, a.a2g));
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    x[e] = sc > 0.0f ? e2m1_value(e2m1_encode(__fdiv_rn(x[e], sc))) * sc : 0.0f;
+                for (int e = 0; e < 16; ++e) x[e] = e2m1_value(nvfp4_act_code(x[e], sc, a.a2g)) * sc;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_bits(x[2 * e]) | (f32_to_f16_bits(x[2 * e + 1]) << 16);
             } else {
@@ -436,7 +435,7 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
     const int sr = wave * SR + (lane & (SR - 1));
     const uint8_t* ass = ascales + (size_t)arow(sr) * (K / 16);
     const uint8_t* bss = wscales + (size_t)weight_row(sr) * (K / 16);
-    const float gscale = KIND == 1 ? W.g13[ex] : W.g2[ex];
+    const float gscale = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;   // weight x activation globals
 
     const int nvi = max(0, min(4, (re - rb - wm * 128 + 31) >> 5));
     const int nc = K / kQK;
@@ -574,12 +573,12 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
             float m = 0.f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
-            const uint32_t sbyte = e4m3_encode_nonneg(__fdiv_rn(m, 6.0f));
+            const uint32_t sbyte = nvfp4_act_scale(m, a.a2g);
             const float sc = e4m3_to_f32(sbyte);
             uint32_t lo = 0u, hi = 0u;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const uint32_t cd = sc > 0.0f ? e2m1_encode(__fdiv_rn(x[e], sc)) : 0u;
+                const uint32_t cd = nvfp4_act_code(x[e], sc, a.a2g);
                 if (e < 8) lo |= cd << (4 * e);
                 else hi |= cd << (4 * (e - 8));
             }

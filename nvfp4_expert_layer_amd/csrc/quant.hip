@@ -8,6 +8,8 @@
 //   weights:      g = amax_tensor / 2688  (1 if amax = 0),   2688 = 6 * 448
 //                 s = E4M3(amax_block / (6 * g)),  c = E2M1(w / (s * g))
 //   activations:  s = E4M3(amax_block / 6),        c = E2M1(x / s)
+//                 (static W4A4: a calibrated global g_a, s = E4M3(amax_block /
+//                 (6 g_a)), c = E2M1(x / (s g_a)), the weight rule's block step)
 // E4M3 and E2M1 round to nearest, ties to the even code, and saturate (448, 6);
 // a block whose scale rounds to 0 gets all-zero codes.
 #include "device_common.h"
@@ -15,16 +17,18 @@
 
 namespace moe {
 
-// One thread per 16-element block.  x: bf16 [R][C]; g: pointer to the global
-// scale (nullptr = 1, the activation rule); gsel: which tensor's g (row / rows_per).
+// One thread per 16-element block.  x: bf16 [R][C]; amax_or_null: per-tensor
+// amax (weights: g = amax / 2688 of tensor row / rows_per_tensor), or nullptr
+// for activations with the global g_act (1 for the dynamic rule).
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(
     const uint16_t* __restrict__ x, long long nblocks, int C, int rows_per_tensor,
-    const float* __restrict__ amax_or_null, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const float* __restrict__ amax_or_null, float g_act, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
     long long b = (long long)blockIdx.x * 256 + threadIdx.x;
     if (b >= nblocks) return;
     const int bpr = C / kBlock;
     const long long row = b / bpr;
-    float g = 1.0f;
+    float g = g_act;
     if (amax_or_null) {
         float amax = amax_or_null[row / rows_per_tensor];
         g = amax > 0.0f ? __fdiv_rn(amax, 2688.0f) : 1.0f;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(
 // product has at most 6 significant bits and lies in f16's normal range.
 template <bool F16>
 __global__ __launch_bounds__(256) void fake_quant_act_kernel(const uint16_t* __restrict__ x, long long nblocks,
-                                                             uint16_t* __restrict__ out) {
+                                                             float g, uint16_t* __restrict__ out) {
     long long b = (long long)blockIdx.x * 256 + threadIdx.x;
     if (b >= nblocks) return;
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + b * kBlock);
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void fake_quant_act_kernel(const uint16_t* __r
     uint32_t o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float lo = nvfp4_fake_quant(f[2 * i], bmax), hi = nvfp4_fake_quant(f[2 * i + 1], bmax);
+        const float lo = nvfp4_fake_quant(f[2 * i], bmax, g), hi = nvfp4_fake_quant(f[2 * i + 1], bmax, g);
         o[i] = F16 ? f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16) : pack_hi16(lo, hi);
     }
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + b * kBlock);
@@ -139,24 +143,25 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_act(const uint16_t* x, int R, int C, uint8_t* codes, uint8_t* scales,
+hipError_t launch_quantize_act(const uint16_t* x, int R, int C, float g, uint8_t* codes, uint8_t* scales,
                                hipStream_t s) {
     long long nb = (long long)R * (C / kBlock);
     if (nb == 0) return hipSuccess;
     hipLaunchKernelGGL(quantize_blocks_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
-                       C, 1, (const float*)nullptr, codes, scales);
+                       C, 1, (const float*)nullptr, g, codes, scales);
     return hipGetLastError();
 }
 
-hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, uint16_t* out, bool f16_out, hipStream_t s) {
+hipError_t launch_fake_quant_act(const uint16_t* x, int R, int C, float g, uint16_t* out, bool f16_out,
+                                 hipStream_t s) {
     long long nb = (long long)R * (C / kBlock);
     if (nb == 0) return hipSuccess;
     if (f16_out)
         hipLaunchKernelGGL(fake_quant_act_kernel<true>, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
-                           out);
+                           g, out);
     else
         hipLaunchKernelGGL(fake_quant_act_kernel<false>, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, x, nb,
-                           out);
+                           g, out);
     return hipGetLastError();
 }
 
@@ -172,7 +177,7 @@ hipError_t launch_quantize_weights(const uint16_t* w, int n, int R, int C, uint8
     long long nb = (long long)n * R * (C / kBlock);
     if (nb > 0)
         hipLaunchKernelGGL(quantize_blocks_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, w, nb,
-                           C, R, (const float*)global, codes, scales);
+                           C, R, (const float*)global, 1.0f, codes, scales);
     hipLaunchKernelGGL(amax_to_global_kernel, dim3((n + 255) / 256), dim3(256), 0, s, global, n);
     return hipGetLastError();
 }

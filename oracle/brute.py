@@ -36,9 +36,10 @@ def dequant_matrix(packed, scales, g):
     return W
 
 
-def fake_quant_row(v):
-    """W4A4 activation quantize-dequantize of one row, by explicit loops.
-    Decisions in fp32 (via struct round trips) like the vectorised oracle."""
+def fake_quant_row(v, g=1.0):
+    """W4A4 activation quantize-dequantize of one row, by explicit loops; g is
+    the static activation global (1: dynamic W4A4).  Decisions in fp32 (via
+    struct round trips) like the vectorised oracle."""
     import struct
 
     def f32(z):
@@ -63,24 +64,30 @@ def fake_quant_row(v):
                 break
         return best
 
+    g = f32(g)
     out = []
     for b0 in range(0, len(v), 16):
         blk = [f32(z) for z in v[b0:b0 + 16]]
         amax = max(abs(z) for z in blk)
-        s = e4m3_vals[rne(f32(amax / f32(6.0)), e4m3_vals)]
+        s = e4m3_vals[rne(f32(amax / f32(6.0 * g)), e4m3_vals)]
+        sg = f32(s * g)
         for z in blk:
-            if s == 0:
+            if sg == 0:
                 out.append(0.0)
                 continue
-            r = f32(z / s)
+            r = f32(z / sg)
             mag = e2m1_vals[rne(abs(r), e2m1_vals)]
-            out.append(-mag * s if (r < 0 and mag != 0) else mag * s)
+            out.append(-mag * s * g if (r < 0 and mag != 0) else mag * s * g)
     return out
 
 
-def layer(x, gate, experts_q, shared_q, top_k, offset, num_local, w4a4=False):
+def layer(x, gate, experts_q, shared_q, top_k, offset, num_local, w4a4=False, act_global=None):
     """x: [T][d] floats; gate: [d][E]; experts_q[l] / shared_q: dicts of
-    packed codes, scales and g for w13 ([2F][d]) and w2 ([d][F])."""
+    packed codes, scales and g for w13 ([2F][d]) and w2 ([d][F]).
+    act_global = (g of h, g of the SwiGLU output) selects static W4A4."""
+    if act_global is not None:
+        w4a4 = True
+    ga = act_global if act_global is not None else (1.0, 1.0)
     T, d, E = len(x), len(x[0]), len(gate[0])
 
     def mlp(h, q):
@@ -93,7 +100,7 @@ def layer(x, gate, experts_q, shared_q, top_k, offset, num_local, w4a4=False):
             usum = sum(W13[F + f][c] * h[c] for c in range(d))
             a.append(gsum / (1.0 + math.exp(-gsum)) * usum if gsum > -700 else 0.0 * usum)
         if w4a4:
-            a = fake_quant_row(a)
+            a = fake_quant_row(a, ga[1])
         return [sum(W2[c][f] * a[f] for f in range(F)) for c in range(d)]
 
     out = [[0.0] * d for _ in range(T)]
@@ -110,7 +117,7 @@ def layer(x, gate, experts_q, shared_q, top_k, offset, num_local, w4a4=False):
             chosen.append(best)
         zmax = logits[chosen[0]]
         den = sum(math.exp(logits[e] - zmax) for e in chosen)
-        h = fake_quant_row(x[t]) if w4a4 else list(x[t])
+        h = fake_quant_row(x[t], ga[0]) if w4a4 else list(x[t])
         for e in chosen:
             lam = e - offset
             if 0 <= lam < num_local:

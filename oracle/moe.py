@@ -26,6 +26,10 @@ Test infrastructure only (see the package docstring).  Source of each step:
     scale) before both GEMMs: the hidden rows before gate/up (routed and shared
     alike) and the SwiGLU output before down.  The router never sees quantized
     activations.
+  * static W4A4 (same page, section "수정 사항": the third fused-MoE backend
+    variant is static NVFP4 W4A4): the same two quantization points, each with a
+    calibrated per-layer activation global g_a fixed ahead of time (act_global
+    = (g_a of h, g_a of the SwiGLU output)), block scale E4M3(amax / (6 g_a)).
 """
 import numpy as np
 
@@ -33,6 +37,7 @@ from . import nvfp4
 
 W4A16 = 0
 W4A4 = 1
+W4A4_STATIC = 2
 
 # Tokens whose k-th and (k+1)-th fp64 logits differ by less than this are
 # reported as ambiguous: any GPU selection that differs from the oracle only
@@ -109,7 +114,16 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_mlp(h, w13, w2, mode):
+def quantize_input(x, mode, act_global):
+    """The activation step before GEMM1 (the identity for W4A16)."""
+    if mode == W4A4:
+        return nvfp4.fake_quant_act(x)
+    if mode == W4A4_STATIC:
+        return nvfp4.fake_quant_act(x, act_global[0])
+    return x
+
+
+def expert_mlp(h, w13, w2, mode, act_global=(1.0, 1.0)):
     """h: fp64 [n, d] (already quantized for W4A4); w13: fp64 [2F, d];
     w2: fp64 [d, F] (dequantized).  Returns fp64 [n, d]."""
     F = w13.shape[0] // 2
@@ -117,6 +131,8 @@ def expert_mlp(h, w13, w2, mode):
     a = silu(u[:, :F]) * u[:, F:]
     if mode == W4A4:
         a = nvfp4.fake_quant_act(a)
+    elif mode == W4A4_STATIC:
+        a = nvfp4.fake_quant_act(a, act_global[1])
     return a @ w2.T
 
 
@@ -127,7 +143,7 @@ def dequant_expert(q):
     return w13, w2
 
 
-def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=None):
+def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=None, act_global=(1.0, 1.0)):
     """The fused MoE layer for one shard.
 
     x       fp64 [T, d]   (bf16 hidden, exactly widened)
@@ -135,6 +151,7 @@ def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=No
     experts callable or list: experts(l) -> quantized dict for local expert l
             (l in [0, num_local), i.e. global id offset + l)
     shared  quantized dict of the shared expert, or None (has_shared = 0)
+    act_global  static W4A4 only: (g_a of h, g_a of the SwiGLU output)
     Returns dict(out fp64 [T, d], routing..., perm...).
     """
     x = np.asarray(x, np.float64)
@@ -142,7 +159,7 @@ def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=No
     r = routing if routing is not None else route(x, gate, top_k)
     lam = shard_filter(r["ids"], offset, num_local)
     pm = permutation(lam, num_local)
-    h = nvfp4.fake_quant_act(x) if mode == W4A4 else x
+    h = quantize_input(x, mode, act_global)
     get = experts if callable(experts) else (lambda l: experts[l])
     out = np.zeros((T, d), dtype=np.float64)
     flatw = r["weights"].reshape(-1)
@@ -153,20 +170,20 @@ def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=No
         pairs = pm["perm"][lo:hi].astype(np.int64)
         tok = pairs // top_k
         w13, w2 = dequant_expert(get(l))
-        y = expert_mlp(h[tok], w13, w2, mode)
+        y = expert_mlp(h[tok], w13, w2, mode, act_global)
         out[tok] += flatw[pairs][:, None] * y       # at most one pair per (token, expert)
     if shared is not None:
         w13, w2 = dequant_expert(shared)
-        out += expert_mlp(h, w13, w2, mode)
+        out += expert_mlp(h, w13, w2, mode, act_global)
     return {"out": out, "ids": r["ids"], "weights": r["weights"], "logits": r["logits"],
             "ambiguous": r["ambiguous"], "local_ids": lam, **pm}
 
 
-def forward_rows(x_rows, routing_rows, experts, shared, top_k, offset, num_local, mode):
+def forward_rows(x_rows, routing_rows, experts, shared, top_k, offset, num_local, mode, act_global=(1.0, 1.0)):
     """Output rows for a subset of tokens, given their routing (ids/weights rows).
     Used to check sampled outputs of large problems one token at a time."""
     x_rows = np.asarray(x_rows, np.float64)
-    h = nvfp4.fake_quant_act(x_rows) if mode == W4A4 else x_rows
+    h = quantize_input(x_rows, mode, act_global)
     get = experts if callable(experts) else (lambda l: experts[l])
     out = np.zeros_like(h)
     for i in range(h.shape[0]):
@@ -174,10 +191,10 @@ def forward_rows(x_rows, routing_rows, experts, shared, top_k, offset, num_local
             lam = int(routing_rows["ids"][i, j]) - offset
             if 0 <= lam < num_local:
                 w13, w2 = dequant_expert(get(lam))
-                out[i] += routing_rows["weights"][i, j] * expert_mlp(h[i:i + 1], w13, w2, mode)[0]
+                out[i] += routing_rows["weights"][i, j] * expert_mlp(h[i:i + 1], w13, w2, mode, act_global)[0]
     if shared is not None:
         w13, w2 = dequant_expert(shared)
-        out += expert_mlp(h, w13, w2, mode)
+        out += expert_mlp(h, w13, w2, mode, act_global)
     return out
 
 

@@ -25,6 +25,11 @@ operations are IEEE single with round-to-nearest-even):
                 c  = E2M1(w / (s * g))            (c = 0 where s = 0)
   activations:  s  = E4M3(amax_block / 6)         (no global scale)
                 c  = E2M1(x / s)
+  static W4A4 activations (a calibrated per-tensor activation global g_a,
+  fixed ahead of time; the page's "static" W4A4 variant names the idea and
+  leaves the rule open -- read as the weight rule's block step with g = g_a):
+                s  = E4M3(amax_block / (6 * g_a))
+                c  = E2M1(x / (s * g_a))          value = c * s * g_a
 """
 import numpy as np
 
@@ -179,11 +184,12 @@ def quantize_weight(w):
     return {"codes": pack_nibbles(codes), "scales": sbytes, "g": np.float32(g)}
 
 
-def quantize_act(x):
-    """Activations [R, C] (fp32 values), blocks of 16 along C, no global scale.
+def quantize_act(x, g=1.0):
+    """Activations [R, C] (fp32 values), blocks of 16 along C; g = 1 (dynamic
+    W4A4, no global scale) or a static activation global g_a (fp32).
     Returns dict(codes=packed uint8 [R, C/2], scales=uint8 [R, C/16])."""
     x32 = np.asarray(x, dtype=np.float32)
-    codes, sbytes = _quantize_rows(x32, np.float32(1.0))
+    codes, sbytes = _quantize_rows(x32, np.float32(g))
     return {"codes": pack_nibbles(codes), "scales": sbytes}
 
 
@@ -196,7 +202,8 @@ def dequantize(codes_packed, scales, g=1.0):
     return v.reshape(R, C) * np.float64(g)
 
 
-def fake_quant_act(x):
-    """Quantize then dequantize activations (the W4A4 activation step)."""
-    q = quantize_act(x)
-    return dequantize(q["codes"], q["scales"], 1.0)
+def fake_quant_act(x, g=1.0):
+    """Quantize then dequantize activations (the W4A4 activation step; g: the
+    static activation global, 1 for dynamic W4A4)."""
+    q = quantize_act(x, g)
+    return dequantize(q["codes"], q["scales"], np.float32(g))

@@ -68,11 +68,12 @@ class Layer:
         return self.experts.slice(offset - self.lo, L)
 
     def run(self, offset, L, has_shared, mode, path=nv.PATH_AUTO, T=None, x=None, out=None, ws=None,
-            ws_fill=None):
+            ws_fill=None, act_global=None):
         w = self.w
+        act_global = w.act_global if act_global is None else act_global
         x = self.x if x is None else x
         T = x.shape[0]
-        p = nv.make_problem(T, w.d, w.F, w.E, w.k, offset, L, has_shared, mode, path)
+        p = nv.make_problem(T, w.d, w.F, w.E, w.k, offset, L, has_shared, mode, path, act_global)
         if ws is None:
             ws = nv.alloc_workspace(p)
         if ws_fill is not None:
@@ -84,17 +85,19 @@ class Layer:
         torch.cuda.synchronize()
         return out
 
-    def oracle_full(self, offset, L, has_shared, mode):
+    def oracle_full(self, offset, L, has_shared, mode, act_global=None):
+        act_global = self.w.act_global if act_global is None else act_global
         return moe.forward(self.x64, self.G64, lambda l: self.oracle_expert(offset + l),
                            self.oracle_expert(self.w.E) if has_shared else None,
-                           self.w.k, offset, L, mode)
+                           self.w.k, offset, L, mode, act_global=act_global)
 
-    def oracle_rows(self, rows, offset, L, has_shared, mode):
+    def oracle_rows(self, rows, offset, L, has_shared, mode, act_global=None):
+        act_global = self.w.act_global if act_global is None else act_global
         xr = self.x64[rows]
         r = moe.route(xr, self.G64, self.w.k)
         return moe.forward_rows(xr, r, lambda l: self.oracle_expert(offset + l),
                                 self.oracle_expert(self.w.E) if has_shared else None,
-                                self.w.k, offset, L, mode), r
+                                self.w.k, offset, L, mode, act_global=act_global), r
 
 
 def rel_err(gpu_bf16, ref64):

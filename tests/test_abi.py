@@ -105,3 +105,21 @@ def test_resolved_path_crossover():
     assert path(1, nv.W4A4, force=nv.PATH_PREFILL) == nv.PATH_PREFILL
     with pytest.raises(nv.MoeNvfp4Error):
         path(64, nv.W4A16, d=100)
+
+
+def test_static_globals_are_validated():
+    # static W4A4 needs finite activation globals in 2^-100..2^100; other modes ignore them
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-35, 1e35):
+        p = nv.make_problem(64, 512, 256, 24, 4, 0, 24, True, nv.W4A4_STATIC, nv.PATH_AUTO, (bad, 1.0))
+        assert nv.moe_nvfp4_validate(p, 1 << 30) == nv.ERR_INVALID_ARG
+        p = nv.make_problem(64, 512, 256, 24, 4, 0, 24, True, nv.W4A4_STATIC, nv.PATH_AUTO, (1.0, bad))
+        assert nv.moe_nvfp4_validate(p, 1 << 30) == nv.ERR_INVALID_ARG
+    p = nv.make_problem(64, 512, 256, 24, 4, 0, 24, True, nv.W4A4_STATIC, nv.PATH_AUTO, (2.0 ** -100, 2.0 ** 100))
+    assert nv.moe_nvfp4_validate(p, 1 << 30) == nv.OK
+    p = nv.make_problem(64, 512, 256, 24, 4, 0, 24, True, nv.W4A4, nv.PATH_AUTO, (0.0, 0.0))
+    assert nv.moe_nvfp4_validate(p, 1 << 30) == nv.OK
+    # the static mode resolves its path like W4A4 and needs the same workspace
+    ps = nv.make_problem(100, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4_STATIC, nv.PATH_AUTO, (0.01, 0.01))
+    pd = nv.make_problem(100, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4)
+    assert nv.moe_nvfp4_resolved_path(ps) == nv.moe_nvfp4_resolved_path(pd) == nv.PATH_PREFILL
+    assert nv.moe_nvfp4_workspace_size(ps) == nv.moe_nvfp4_workspace_size(pd)

@@ -173,7 +173,8 @@ def full_layer(name):
     return lay
 
 
-FULL = ["decode_shard0_w4a16", "shard1_w4a4_t512", "prefill_all_w4a4", "prefill_zipf_shard0_w4a16"]
+FULL = ["decode_shard0_w4a16", "shard1_w4a4_t512", "shard1_w4a4_static_t512", "prefill_all_w4a4",
+        "prefill_zipf_shard0_w4a16"]
 
 
 @pytest.mark.parametrize("name", FULL)

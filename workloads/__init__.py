@@ -22,6 +22,7 @@ import torch
 
 W4A16 = 0
 W4A4 = 1
+W4A4_STATIC = 2
 
 # Zipf exponent of the skewed-routing prefill workload, and the bias scale that
 # gives its 10 hottest experts ~50% of the T*k assignments.  ZIPF_ALPHA was
@@ -49,6 +50,7 @@ class Workload:
     weight_seed: int
     router: str = "std"        # "std": gate N(0, gate_std); "unit": N(0, 1/sqrt(d)); "zipf"
     gate_std: float = 0.02
+    act_global: tuple = (1.0, 1.0)   # static W4A4: activation globals of h and of the SwiGLU output
     note: str = field(default="", compare=False)
 
 
@@ -64,6 +66,13 @@ WORKLOADS = {
                                  offset=160, L=160, has_shared=False, mode=W4A4,
                                  hidden_seed=102, gate_seed=1234, weight_seed=1234,
                                  note="second shard (experts 160-319), W4A4 dynamic"),
+    # the same shard in static W4A4: fixed activation globals amax / (6 * 448)
+    # for calibrated amax 5 (the N(0, 1) hidden rows) and 12 (the SwiGLU output)
+    "shard1_w4a4_static_t512": Workload("shard1_w4a4_static_t512", T=512, d=4096, F=1024, E=320, k=8,
+                                        offset=160, L=160, has_shared=False, mode=W4A4_STATIC,
+                                        hidden_seed=102, gate_seed=1234, weight_seed=1234,
+                                        act_global=(0.0018601190531626344, 0.004464285913854837),
+                                        note="second shard, static W4A4 (calibrated activation globals)"),
     "prefill_all_w4a4": Workload("prefill_all_w4a4", T=8192, d=4096, F=1024, E=320, k=8,
                                  offset=0, L=320, has_shared=True, mode=W4A4,
                                  hidden_seed=103, gate_seed=103, weight_seed=1234,
