@@ -56,12 +56,12 @@ constexpr int kPN = 256;                       // tile weight rows
 constexpr int kPK = 64;                        // K per stage
 constexpr int kPWaves = 8;
 constexpr int kPA = kPM * kPK * 2;             // bytes of one A stage (32 KB)
-constexpr int kPASlots = 4;
-constexpr int kPRawC = kPN * (kPK / 2);        // raw codes of one step (8 KB: 32 B per weight row)
-constexpr int kPRaw = kPRawC + kPN * 4;        // + raw scales (1 KB: 4 B per weight row)
+constexpr int kPASlots = 3;
+constexpr int kPRawC = kPN * 64;               // raw codes of a two-step chunk (16 KB: 64 B per weight row)
+constexpr int kPRaw = kPRawC + kPN * 8;        // + raw scales (2 KB: 8 B per weight row)
 constexpr int kPRSlots = 3;
-constexpr int kPOffR = kPASlots * kPA;         // LDS map: A[4] | raw[3]
-constexpr int kPLds = kPOffR + kPRSlots * kPRaw;   // 155 KB
+constexpr int kPOffR = kPASlots * kPA;         // LDS map: A[3] | raw[3]
+constexpr int kPLds = kPOffR + kPRSlots * kPRaw;   // 150 KB
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -74,10 +74,11 @@ __device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(
 // lanes of a 16-byte access per cycle.
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
 
-// Raw code rows: the two 16-byte halves of weight row r are stored swapped when
-// rawf(r) = 1, so that 32 lanes reading one half of 32 consecutive rows
-// (32-byte stride) hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int rawf(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// 16-byte unit u of a 64-byte raw code row r (two 64-k steps): 32 lanes reading
+// one unit of 32 consecutive rows, or 8 / 16 consecutive rows' same unit, hit
+// distinct bank groups whether the LDS serves 8 or 16 lanes of a 16-byte access
+// per cycle.
+__device__ __forceinline__ int cwz(int r, int u) { return r * 64 + ((u ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4); }
 
 template <int MODE>
 __device__ __forceinline__ f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
@@ -134,36 +135,42 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
                   (((lane & 7) ^ (lane >> 3) ^ (q & 1)) << 3);
     }
 
-    // ---- raw weight sources ----
-    // codes: wave w, lane i -> weight row r = 32 w + i/2; it copies the half
-    // (i%2) ^ rawf(r) of the row's 32 code bytes of the step to raw + 32 r + 16 (i%2)
-    // = raw + 1024 w + 16 i.  scales: lane i < 32 -> row 32 w + i, its 4 scale
-    // bytes of the step at raw + 8 KB + 4 r = raw + 8 KB + 128 w + 4 i.
+    // ---- raw weight sources: two 64-k steps per chunk ----
+    // codes: load q (0, 1) of wave w fills rows 16 (2w + q) .. +16 of the chunk's
+    // [256][64 B] code tile (1 KB, lane i at byte 16 i): lane i -> row r =
+    // 16 (2w + q) + i/4, 16-byte slot i%4 of the row, which holds unit
+    // (i%4) ^ g(r) (cwz).  scales: lane i -> row 32 w + i/2, dword i%2 (the
+    // chunk's two steps) at raw + 16 KB + 8 r + 4 (i%2) = raw + 16 KB + 256 w + 4 i.
     auto weight_row = [&](int r) {
         if (KIND == 1) return (r < 128 ? 0 : F - 128) + nt * 128 + r;
         return min(nt * kPN + r, d - 1);                 // columns past d: any valid row
     };
     const uint8_t* wcodes = KIND == 1 ? W.w13 + ex * (size_t)(2 * F) * (d / 2) : W.w2 + ex * (size_t)d * (F / 2);
     const uint8_t* wscales = KIND == 1 ? W.w13_s + ex * (size_t)(2 * F) * (d / 16) : W.w2_s + ex * (size_t)d * (F / 16);
-    const int crow = wave * 32 + (lane >> 1);
-    const uint8_t* csrc = wcodes + (size_t)weight_row(crow) * (K / 2) + ((lane & 1) ^ rawf(crow)) * 16;
-    const uint8_t* ssrc = wscales + (size_t)weight_row(wave * 32 + (lane & 31)) * (K / 16);
+    const uint8_t* csrc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int r = (wave * 2 + q) * 16 + (lane >> 2);
+        csrc[q] = wcodes + (size_t)weight_row(r) * (K / 2) + (((lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+    }
+    const uint8_t* ssrc = wscales + (size_t)weight_row(wave * 32 + (lane >> 1)) * (K / 16) + (lane & 1) * 4;
     const float gscale = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;   // weight x activation globals
 
     // valid 32-row blocks of this wave (rows past re are padding)
     const int nvi = max(0, min(4, (re - rb - wm * 128 + 31) >> 5));
     const bool colv = KIND == 1 || nt * kPN + wn * (32 * NJ) < d;
-    const int nk = K / kPK;
+    const int nk = K / kPK, nc = nk / 2;             // K % 128 == 0: whole chunks
 
-    // Direct loads per wave per step, in this order: one raw code load, one raw
-    // scale load (lanes < 32), then NA A loads.
-    auto issue_raw = [&](int ks, int slot) {
+    // Direct loads per wave: NA A loads per step; at even steps also the next
+    // chunk's two code loads and one scale load.
+    auto issue_raw = [&](int c, int slot) {
         uint8_t* rbase = smem + kPOffR + slot * kPRaw;
-        __builtin_amdgcn_global_load_lds((const void*)(csrc + ks * (kPK / 2)), (lds_void_t*)(rbase + wave * 1024),
-                                         16, 0, 0);
-        if (lane < 32)
-            __builtin_amdgcn_global_load_lds((const void*)(ssrc + ks * (kPK / 16)),
-                                             (lds_void_t*)(rbase + kPRawC + wave * 128), 4, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            __builtin_amdgcn_global_load_lds((const void*)(csrc[q] + c * 64),
+                                             (lds_void_t*)(rbase + (wave * 2 + q) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ssrc + c * 8), (lds_void_t*)(rbase + kPRawC + wave * 256), 4,
+                                         0, 0);
     };
     auto issue_a = [&](int ks, int slot) {
         uint8_t* abase = smem + slot * kPA + wave * NA * 1024;
@@ -186,84 +193,85 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
     // 32 j + l%32
     const int arow0 = wm * 128 + (lane & 31);
     const int h = lane >> 5;
-    int roff[NJ], soff[NJ];
+    int brow[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int br = (KIND == 1 ? j * 128 + wn * 32 : wn * 64 + j * 32) + (lane & 31);
-        roff[j] = br * 32 + ((h ^ rawf(br)) << 4);
-        soff[j] = kPRawC + br * 4;
-    }
+    for (int j = 0; j < NJ; ++j) brow[j] = (KIND == 1 ? j * 128 + wn * 32 : wn * 64 + j * 32) + (lane & 31);
 
-    // Pipeline, step ks (A slot ks % 4, raw slot ks % 3):
-    //   issue raw(ks+2) and A(ks+3) into the slots freed by the last barrier;
-    //   read this step's raw codes and scales, decode each MFMA's weight operand
-    //   in registers just before it, A operands double-buffered in registers;
-    //   end: wait until raw(ks+1) (and everything issued before it, A(ks+1)
-    //   included) has landed: only A(ks+2), raw(ks+2), A(ks+3) may still be in
-    //   flight (NA + 2 + NA = 10 loads); LDS reads done; workgroup barrier.
+    // Pipeline, step ks (A slot ks % 3; chunk ks/2 in raw slot (ks/2) % 3):
+    //   issue A(ks+2) and, at even steps, chunk ks/2 + 1, into slots freed by
+    //   the last barrier (past the end both are clamped: re-loads of valid data
+    //   into free slots, so every step issues the same loads);
+    //   read this step's raw codes (unit 2 (ks%2) + h of the row) and scales,
+    //   decode each MFMA's weight operand in registers just before it, A
+    //   operands double-buffered in registers;
+    //   end: wait until only this step's own loads may be in flight (so A(ks+1)
+    //   and the chunk of step ks+1 have landed); LDS reads done; barrier.
     // Nothing in the loop loads into registers from global memory, so every wait
-    // on the direct loads is this explicit one.  Past the end the loads are
-    // clamped to the last step (re-loads of valid data into free slots).
-    auto kloop = [&](auto nv_c) {
+    // on the direct loads is this explicit one.
+    auto step = [&](auto nv_c, auto st_c, int ks, int as, int rs) {
         constexpr int NV = decltype(nv_c)::value;
-        int rs = 0;                                        // raw slot of step ks
-        for (int ks = 0; ks < nk; ++ks) {
-            const int rs2 = rs == 0 ? 2 : rs - 1;          // (ks + 2) % 3
-            issue_raw(min(ks + 2, nk - 1), rs2);
-            issue_a(min(ks + 3, nk - 1), (ks + 3) & 3);
-            if (NV > 0) {
-                const uint8_t* As = smem + (ks & 3) * kPA;
-                const uint8_t* Rs = smem + kPOffR + rs * kPRaw;
-                u32x4_t rc[NJ];
-                uint32_t sc[NJ];
+        constexpr int ST = decltype(st_c)::value;      // ks % 2
+        issue_a(min(ks + 2, nk - 1), as == 0 ? 2 : as - 1);
+        if (ST == 0) issue_raw(min(ks / 2 + 1, nc - 1), rs == 2 ? 0 : rs + 1);
+        if (NV > 0) {
+            const uint8_t* As = smem + as * kPA;
+            const uint8_t* Rs = smem + kPOffR + rs * kPRaw;
+            u32x4_t rc[NJ];
+            uint32_t sc[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                rc[j] = *reinterpret_cast<const u32x4_t*>(Rs + cwz(brow[j], 2 * ST + h));
+                sc[j] = *reinterpret_cast<const uint32_t*>(Rs + kPRawC + brow[j] * 8 + ST * 4) >> (16 * h);
+            }
+            u32x4_t av[2][4];
+            auto frag = [&](int kk, int f) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    av[f][i] = *reinterpret_cast<const u32x4_t*>(As + swz(arow0 + i * 32, 4 * h + kk));
+            };
+            frag(0, 0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) frag(kk + 1, (kk + 1) & 1);
+                u32x4_t bv[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    rc[j] = *reinterpret_cast<const u32x4_t*>(Rs + roff[j]);
-                    sc[j] = *reinterpret_cast<const uint32_t*>(Rs + soff[j]) >> (16 * h);
-                }
-                u32x4_t av[2][4];
-                auto frag = [&](int kk, int f) {
-#pragma unroll
-                    for (int i = 0; i < NV; ++i)
-                        av[f][i] = *reinterpret_cast<const u32x4_t*>(As + swz(arow0 + i * 32, 4 * h + kk));
-                };
-                frag(0, 0);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    if (kk < 3) frag(kk + 1, (kk + 1) & 1);
-                    u32x4_t bv[NJ];
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const uint32_t sbyte = (sc[j] >> (8 * (kk >> 1))) & 0xFFu;
-                        if constexpr (MODE == 1) {
-                            const _Float16 s = (_Float16)e4m3_to_f32(sbyte);
-                            bv[j] = dequant8_f16(rc[j][kk], f16x2_t{s, s});
-                        } else {
-                            bv[j] = dequant8_bf16(rc[j][kk], e4m3_to_f32(sbyte));
-                        }
+                    const uint32_t sbyte = (sc[j] >> (8 * (kk >> 1))) & 0xFFu;
+                    if constexpr (MODE == 1) {
+                        const _Float16 s = (_Float16)e4m3_to_f32(sbyte);
+                        bv[j] = dequant8_f16(rc[j][kk], f16x2_t{s, s});
+                    } else {
+                        bv[j] = dequant8_bf16(rc[j][kk], e4m3_to_f32(sbyte));
                     }
-#pragma unroll
-                    for (int i = 0; i < NV; ++i)
-#pragma unroll
-                        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<MODE>(av[kk & 1][i], bv[j], acc[i][j]);
                 }
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32<MODE>(av[kk & 1][i], bv[j], acc[i][j]);
             }
-            // Written out because __syncthreads() would also wait for every
-            // outstanding load (vmcnt(0)) and drain the pipeline; the memory
-            // clobber keeps the compiler from moving LDS accesses across it.
-            asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        // Written out because __syncthreads() would also wait for every
+        // outstanding load (vmcnt(0)) and drain the pipeline; the memory
+        // clobber keeps the compiler from moving LDS accesses across it.
+        if (ST == 0) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // NA + 3
+        else asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");           // NA
+    };
+    auto kloop = [&](auto nv_c) {
+        int as = 0, rs = 0;                                // A slot of step ks, raw slot of its chunk
+        for (int ks = 0; ks < nk; ks += 2) {
+            step(nv_c, std::integral_constant<int, 0>{}, ks, as, rs);
+            as = as == 2 ? 0 : as + 1;
+            step(nv_c, std::integral_constant<int, 1>{}, ks + 1, as, rs);
+            as = as == 2 ? 0 : as + 1;
             rs = rs == 2 ? 0 : rs + 1;
         }
     };
 
-    // prologue: A(0), raw(0), A(1), raw(1), A(2) -- the steady-state issue order
-    // (raw(m), A(m+1)) preceded by A(0); then wait as at the end of a step
+    // prologue: A(0), A(1), chunk 0; all landed before the loop
     issue_a(0, 0);
+    issue_a(1, 1);
     issue_raw(0, 0);
-    issue_a(min(1, nk - 1), 1);
-    issue_raw(min(1, nk - 1), 1);
-    issue_a(min(2, nk - 1), 2);
-    asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     switch (colv ? nvi : 0) {
         case 4: kloop(std::integral_constant<int, 4>{}); break;
         case 3: kloop(std::integral_constant<int, 3>{}); break;
