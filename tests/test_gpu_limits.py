@@ -1,0 +1,75 @@
+"""The library's stated limits, on the GPU against the oracle:
+  * d = 16384 (the largest model width) with F = 128, and F = 16384 with
+    d = 128: the weight-streaming kernels then stage the token rows in
+    chunks (the whole K no longer fits in LDS), and the tiled kernels run 256
+    K steps and the widest column grids;
+  * E = 1024 experts with top-32 (the largest routing), through the few-token
+    and the many-token selection kernels and a full layer over all 1024 local
+    experts (every permutation counter at its widest).
+Full outputs within 1e-2 (W4A16) / 3e-2 (W4A4); routing ids, counts, offsets
+and permutation bit-exact."""
+import pytest
+
+import nvfp4_expert_layer_amd as nv
+import workloads
+from tests.gpu_helpers import Layer, log, rel_err, require_gpu, tol
+from tests.test_gpu_route import _check
+
+pytestmark = pytest.mark.gpu
+
+W4A16, W4A4 = workloads.W4A16, workloads.W4A4
+
+WIDE_D = workloads.Workload("max_d", T=40, d=16384, F=128, E=6, k=2, offset=0, L=6, has_shared=True,
+                            mode=W4A16, hidden_seed=61, gate_seed=61, weight_seed=61, gate_std=0.01)
+WIDE_F = workloads.Workload("max_f", T=40, d=128, F=16384, E=6, k=2, offset=1, L=4, has_shared=True,
+                            mode=W4A16, hidden_seed=62, gate_seed=62, weight_seed=62, gate_std=0.1)
+MANY_E = workloads.Workload("max_e", T=24, d=128, F=128, E=1024, k=32, offset=0, L=1024, has_shared=True,
+                            mode=W4A16, hidden_seed=63, gate_seed=63, weight_seed=63, gate_std=0.2)
+
+_layers = {}
+
+
+def get(w):
+    if w.name not in _layers:
+        _layers[w.name] = Layer(w)
+    return _layers[w.name]
+
+
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
+@pytest.mark.parametrize("wl", [WIDE_D, WIDE_F], ids=["d16384", "F16384"])
+def test_widest_layers(wl, path, mode):
+    require_gpu()
+    lay = get(wl)
+    w = lay.w
+    log(f"{w.name}: d={w.d} F={w.F} mode={mode} path={path}")
+    out = lay.run(w.offset, w.L, w.has_shared, mode, path)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, mode)["out"]
+    err = rel_err(out, ref)
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(mode)
+
+
+@pytest.mark.parametrize("T", [40, 1100])
+def test_route_1024_experts_top32(T):
+    require_gpu()
+    w = workloads.replace(MANY_E, T=T, d=256)
+    log(f"route E=1024 k=32 T={T}")
+    x = workloads.gen_hidden(w, "cuda")
+    G = workloads.gen_gate(w, "cuda")
+    amb, diff, P = _check(x, G, w, 100, 900, True)
+    log(f"  ambiguous {amb}, differing {diff}, local pairs {P}")
+    assert P > 0
+
+
+@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
+def test_layer_1024_local_experts_top32(path):
+    require_gpu()
+    lay = get(MANY_E)
+    w = lay.w
+    log(f"E=1024 k=32 full layer, path={path}")
+    out = lay.run(w.offset, w.L, w.has_shared, W4A16, path)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, W4A16)["out"]
+    err = rel_err(out, ref)
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(W4A16)
