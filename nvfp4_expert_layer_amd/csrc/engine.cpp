@@ -64,7 +64,7 @@ int resolve_path(const moe_nvfp4_problem& p) {
 struct Plan {
     int KS = 1, path = 1, BM = 16, max_tiles = 0, nblk = 0;
     size_t rows = 0;  // rows of the expanded (pair + shared) activation space
-    size_t part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
+    size_t part, xn2, gn2, mlog, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
         ntiles, perm, inv, hq, act, Y, total;
 };
 
@@ -113,6 +113,8 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.part = take((size_t)pl.KS * T * E * 4);
     pl.xn2 = take((size_t)pl.KS * T * 8);
     pl.gn2 = take((size_t)pl.KS * E * 8);
+    const bool micro = T >= 1 && T <= (size_t)moe::router_micro_tokens();
+    pl.mlog = take(micro ? T * E * 8 : 0);              // fp64 logits of the few-token routing
     pl.topk_ids = take(T * k * 4);
     pl.topk_w = take(T * k * 4);
     pl.local_ids = take(T * k * 4);
@@ -194,8 +196,6 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     r.topk_ids = ids_out ? ids_out : at<int32_t>(ws, pl.topk_ids);
     r.topk_w = w_out ? w_out : at<float>(ws, pl.topk_w);
     r.local_ids = at<int32_t>(ws, pl.local_ids);
-    int st = hip_status(moe::launch_router(r, s), "router launch");
-    if (st) return st;
     moe::PermArgs q{};
     q.local_ids = r.local_ids; q.T = p.num_tokens; q.topk = p.top_k; q.L = p.num_local_experts;
     q.has_shared = p.has_shared; q.BM = pl.BM; q.max_tiles = pl.max_tiles;
@@ -204,6 +204,10 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     q.offsets = offsets_out ? offsets_out : at<int32_t>(ws, pl.offsets);
     q.tiles = at<int4>(ws, pl.tiles); q.ntiles = at<int32_t>(ws, pl.ntiles);
     q.perm = perm_out ? perm_out : at<int32_t>(ws, pl.perm); q.inv = at<int32_t>(ws, pl.inv);
+    if (p.num_tokens >= 1 && p.num_tokens <= moe::router_micro_tokens())
+        return hip_status(moe::launch_route_micro(r, q, at<double>(ws, pl.mlog), s), "routing launch");
+    int st = hip_status(moe::launch_router(r, s), "router launch");
+    if (st) return st;
     return hip_status(moe::launch_permute(q, s), "permutation launch");
 }
 

@@ -74,6 +74,8 @@ struct CombineArgs {
 
 int router_ksplit(int T, int E, int d);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+int router_micro_tokens();                        // T up to which routing takes the two-launch path
+hipError_t launch_route_micro(const RouterArgs& a, const PermArgs& q, double* logits, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int R, int C, float g, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);

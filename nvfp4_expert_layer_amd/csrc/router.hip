@@ -609,12 +609,11 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
     scan_and_emit_tiles(total, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, nullptr);
 }
 
-// All three permutation steps in one workgroup, for T <= kPermBlock.
-__global__ __launch_bounds__(1024) void perm_small_kernel(
-    const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared, int BM,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
-    int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-    extern __shared__ uint32_t masks[];                    // [L][kPermBlock/32]
+// All three permutation steps in one workgroup of 1024 threads, for T <= kPermBlock.
+__device__ void perm_small_body(const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared,
+                                int BM, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                int4* __restrict__ tiles, int32_t* __restrict__ ntiles, int max_tiles,
+                                int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* masks) {
     __shared__ int32_t s_off[1024];
     constexpr int W = kPermBlock / 32;
     const int tid = threadIdx.x;
@@ -644,6 +643,137 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
         }
         inv[p] = pos;
     }
+}
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(
+    const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared, int BM,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
+    int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    extern __shared__ uint32_t masks[];                    // [L][kPermBlock/32]
+    perm_small_body(local_ids, T, topk, L, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, perm, inv,
+                    masks);
+}
+
+// ---------------------------------------------------------------------------
+// Few tokens (T <= kMicroTokens): routing in two launches.  With so few rows
+// the logits are computed exactly in fp64 (bf16 x bf16 products are exact;
+// one wave sums an expert's products for every token in a fixed order), so
+// the selection needs no error bounds or candidate re-scoring; the second
+// kernel selects the top-k of each token (a wave per token), forms the
+// weights and the shard filter, and builds the permutation in the same
+// workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kMicroTokens = 16;
+
+// logits [T][E] fp64: workgroup e takes expert e; thread i multiplies the
+// 8-element pieces i, i + 256, ... of the gate row and of every token's row
+// (all of a piece's loads issued together), a fixed xor butterfly sums each
+// wave, and the four wave sums are added in wave order.
+__global__ __launch_bounds__(256) void router_micro_logits_kernel(const uint16_t* __restrict__ X,
+                                                                  const uint16_t* __restrict__ G, int T, int E,
+                                                                  int d, double* __restrict__ logits) {
+    __shared__ double s_part[4][kMicroTokens];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = blockIdx.x;
+    const uint16_t* g = G + (size_t)e * d;
+    double acc[kMicroTokens];
+#pragma unroll
+    for (int t = 0; t < kMicroTokens; ++t) acc[t] = 0.0;
+    for (int c = tid * 8; c < d; c += 256 * 8) {
+        const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(g + c);
+        u32x4_t xv[kMicroTokens];
+#pragma unroll
+        for (int t = 0; t < kMicroTokens; ++t)
+            if (t < T) xv[t] = *reinterpret_cast<const u32x4_t*>(X + (size_t)t * d + c);
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        double gf[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            gf[2 * q] = (double)__uint_as_float(gw[q] << 16);
+            gf[2 * q + 1] = (double)__uint_as_float(gw[q] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int t = 0; t < kMicroTokens; ++t) {
+            if (t < T) {
+                const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[t] = fma((double)__uint_as_float(xw[q] << 16), gf[2 * q], acc[t]);
+                    acc[t] = fma((double)__uint_as_float(xw[q] & 0xFFFF0000u), gf[2 * q + 1], acc[t]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kMicroTokens; ++t) {
+        if (t < T) {
+            const double v = wave_sum_f64(acc[t]);
+            if (lane == 0) s_part[wave][t] = v;
+        }
+    }
+    __syncthreads();
+    if (tid < T) logits[(size_t)tid * E + e] = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+}
+
+// top-k per token (wave t < T; experts e = lane + 64 s, s < EPL): k rounds of
+// (wave max of the score, then the lowest id holding it); softmax over the k
+// in fp64; then the permutation of all T * k pairs by the whole workgroup.
+template <int EPL>
+__global__ __launch_bounds__(1024) void router_micro_select_kernel(
+    const double* __restrict__ logits, int T, int E, int topk, int offset, int L, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int32_t* __restrict__ local_ids, int has_shared, int BM,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
+    int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    extern __shared__ uint32_t masks[];                  // [L][kPermBlock/32]
+    __shared__ int32_t s_id[kMicroTokens][32];
+    __shared__ double s_sc[kMicroTokens][32];
+    __shared__ int32_t s_lam[kMicroTokens * 32];        // local ids, [T][k]
+    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
+    if (t < T) {
+        double v[EPL];
+#pragma unroll
+        for (int s = 0; s < EPL; ++s) {
+            const int e = lane + 64 * s;
+            v[s] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+        }
+        for (int r = 0; r < topk; ++r) {
+            // this lane's best (largest score; the lowest id among equal scores)
+            double m = v[0];
+            int me = lane;
+#pragma unroll
+            for (int s = 1; s < EPL; ++s)
+                if (v[s] > m) { m = v[s]; me = lane + 64 * s; }
+            double M = m;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+            int id = (m == M && me < E) ? me : 0x7FFFFFFF;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) id = min(id, __shfl_xor(id, o, 64));
+            if ((id & 63) == lane) {
+#pragma unroll
+                for (int s = 0; s < EPL; ++s)
+                    if (lane + 64 * s == id) v[s] = -INFINITY;
+            }
+            if (lane == 0) {
+                s_id[t][r] = id;
+                s_sc[t][r] = M;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();                 // (a wave's LDS accesses complete in order)
+        const double my = lane < topk ? s_sc[t][lane] : 0.0;
+        const double z = lane < topk ? exp(my - s_sc[t][0]) : 0.0;
+        const double zs = wave_sum_f64(z);
+        if (lane < topk) {
+            const int my_id = s_id[t][lane];
+            const size_t o = (size_t)t * topk + lane;
+            topk_ids[o] = my_id;
+            topk_w[o] = (float)(z / zs);
+            const int lam = my_id - offset;
+            local_ids[o] = s_lam[o] = (lam >= 0 && lam < L) ? lam : -1;
+        }
+    }
+    __syncthreads();                                     // every token's local ids are in LDS
+    perm_small_body(s_lam, T, topk, L, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, perm, inv, masks);
 }
 
 // ---------------------------------------------------------------------------
@@ -705,6 +835,22 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k, g2, dim3(kSelThreads), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
                            a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
     }
+    return hipGetLastError();
+}
+
+int router_micro_tokens() { return kMicroTokens; }
+
+hipError_t launch_route_micro(const RouterArgs& a, const PermArgs& q, double* logits, hipStream_t s) {
+    if (a.T < 1 || a.T > kMicroTokens) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(router_micro_logits_kernel, dim3(a.E), dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, logits);
+    const size_t lds = (size_t)q.L * (kPermBlock / 32) * sizeof(uint32_t);
+    auto k = a.E <= 128 ? router_micro_select_kernel<2>
+             : a.E <= 320 ? router_micro_select_kernel<5>
+             : a.E <= 512 ? router_micro_select_kernel<8>
+                          : router_micro_select_kernel<kMaxExperts / 64>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(1024), lds, s, logits, a.T, a.E, a.topk, a.offset, a.L, a.topk_ids,
+                       a.topk_w, a.local_ids, q.has_shared, q.BM, q.counts, q.offsets, q.tiles, q.ntiles,
+                       q.max_tiles, q.perm, q.inv);
     return hipGetLastError();
 }
 

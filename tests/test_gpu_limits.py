@@ -50,7 +50,7 @@ def test_widest_layers(wl, path, mode):
     assert err <= tol(mode)
 
 
-@pytest.mark.parametrize("T", [40, 1100])
+@pytest.mark.parametrize("T", [3, 16, 40, 1100])          # few-token, workgroup-per-token, wave-per-token selection
 def test_route_1024_experts_top32(T):
     require_gpu()
     w = workloads.replace(MANY_E, T=T, d=256)

@@ -117,3 +117,21 @@ def test_route_empty_batch():
     nv.moe_nvfp4_route(p, x if x.numel() else g, g, ws, None, None, counts, offsets, None)
     torch.cuda.synchronize()
     assert not counts.any().item() and not offsets.any().item()
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 17])
+def test_route_few_tokens_both_sides_of_the_exact_fp64_path(T):
+    """Up to 16 tokens the logits are computed exactly in fp64 (no bounds, no
+    re-scoring); 17 tokens take the certified bf16-MFMA path."""
+    require_gpu()
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
+    log(f"route few tokens T={T}")
+    x = workloads.gen_hidden(w, "cuda")
+    if T >= 2:
+        x[1] = 0                                           # a zero token: ids 0..k-1, equal weights
+    G = workloads.gen_gate(w, "cuda")
+    amb, diff, P = _check(x, G, w, w.offset, w.L, w.has_shared)
+    if T >= 2:
+        ids, wts, *_ = _route_gpu(x, G.t().contiguous(), w, w.offset, w.L, w.has_shared)
+        assert ids[1].tolist() == list(range(w.k))
+        assert np.allclose(wts[1], 1.0 / w.k, rtol=0, atol=1e-7)
