@@ -48,10 +48,17 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "device_common.h", "kernels.h"],
 
 
 def kernel_source_hash(path):
+    """Hash of what the path's GEMM kernels are built from: their source file,
+    the device helpers, and the argument structs they receive (kernels.h's
+    host-side declarations are left out: adding a launcher changes no kernel)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[path]:
         with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+            text = fh.read()
+        if f == "kernels.h":
+            t = text.decode()
+            text = t[t.index("struct ExpertWeights"):t.index("struct CombineArgs")].encode()
+        h.update(text)
     return h.hexdigest()[:16]
 
 
