@@ -1,20 +1,25 @@
 // Tiled expert GEMMs for many tokens per expert (prefill), gfx950.
 //
 // A tile is 256 pair rows of one expert group (a local expert, or the shared
-// expert over all tokens) x 256 weight rows, K staged 64 at a time.  Eight
+// expert over all tokens) x 256 weight rows, K advanced 64 at a time.  Eight
 // waves as 2 (rows) x 4 (weight rows); a wave owns 128 x 64 of the tile as
-// 4 x 2 blocks of 32x32x16 MFMAs with fp32 accumulation.  LDS (155 KB of the
-// CU's 160 KB):
-//   A ring, 4 slots of [256 rows][64] 16-bit activations, copied straight from
-//     global memory (global_load_lds_dwordx4, no registers), gathered through
-//     the permutation for GEMM1; the eight 16-byte chunks of a row are
-//     XOR-swizzled by the row so that a 32-row operand read is conflict-free;
-//   raw ring, 3 slots of the 256 weight rows' NVFP4 codes (32 bytes a row) and
-//     E4M3 block scales (4 bytes a row) for the step, copied the same way.
+// 4 x 2 blocks of 32x32x16 MFMAs with fp32 accumulation.  Two kernels:
+//
+// pf_gemm_kernel (16-bit activations).  LDS (150 KB of the CU's 160 KB):
+//   A ring, 3 slots of [256 rows][64] 16-bit activations, two steps ahead,
+//     copied straight from global memory (global_load_lds_dwordx4, no
+//     registers), gathered through the permutation for GEMM1; the eight
+//     16-byte chunks of a row are XOR-swizzled by the row so that a 32-row
+//     operand read is conflict-free;
+//   raw ring, 3 slots of the 256 weight rows' NVFP4 codes (64 bytes a row) and
+//     E4M3 block scales (8 bytes a row) for two steps, copied the same way.
 // Every wave decodes its own weight operand from the raw ring into registers:
 // code * block scale is exact in 16 bits (at most 6 significant bits).  The
 // weight tile is never written back to LDS, so the LDS carries only the A
 // operand reads and the two rings' fills.
+//
+// pf4_gemm_kernel (W4A4 with NVFP4 activations; see its own comment): both
+// operands arrive raw, 256 k per chunk, and both are decoded per wave.
 //
 // K order inside a step: the MFMA sums over its 16 k in any order as long as
 // both operands use the same one.  Lane half h of MFMA kk (0..3) takes the
@@ -621,6 +626,8 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
     }
 }
 
+// 8 waves (2 per SIMD, 128 x 64 wave tiles); the kernel also builds with 4
+// (one per SIMD, 128 x 128 wave tiles), measured slower.
 constexpr int kQWaves = 8;
 
 template <int KIND>
