@@ -19,6 +19,7 @@ headline workload (the T=64 expert-shard decode step), with:
 --all prints one line per workload instead (a report, not the default line).
 """
 import argparse
+import re
 import ctypes
 import hashlib
 import json
@@ -55,10 +56,12 @@ def kernel_source_hash(path):
     for f in KERNEL_SOURCES[path]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             text = fh.read()
+        t = text.decode()
         if f == "kernels.h":
-            t = text.decode()
-            text = t[t.index("struct ExpertWeights"):t.index("struct CombineArgs")].encode()
-        h.update(text)
+            t = t[t.index("struct ExpertWeights"):t.index("struct CombineArgs")]
+        t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)          # comments do not change a kernel
+        t = re.sub(r"//[^\n]*", "", t)
+        h.update(t.encode())
     return h.hexdigest()[:16]
 
 
