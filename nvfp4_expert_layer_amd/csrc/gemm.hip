@@ -26,9 +26,32 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             s[2 * q + 1] = fmaf(w, bf16_bits_to_f32(yw[q] >> 16), s[2 * q + 1]);
         }
     };
-    for (int j = 0; j < a.topk; ++j) {
-        const int row = a.inv[(size_t)t * a.topk + j];
-        if (row >= 0) add_row((size_t)row, a.topk_w[(size_t)t * a.topk + j]);
+    // slots in groups of 8: the group's row indices and weights first, then its
+    // expert rows, so each group costs two memory round trips, not 2 per slot;
+    // the sum still runs in slot order
+    for (int j0 = 0; j0 < a.topk; j0 += 8) {
+        int row[8];
+        float w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int j = j0 + q;
+            row[q] = j < a.topk ? a.inv[(size_t)t * a.topk + j] : -1;
+            w[q] = j < a.topk ? a.topk_w[(size_t)t * a.topk + j] : 0.f;
+        }
+        u32x4_t y[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (row[q] >= 0) y[q] = *reinterpret_cast<const u32x4_t*>(a.Y + (size_t)row[q] * a.d + c0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (row[q] < 0) continue;
+            const uint32_t yw[4] = {y[q].x, y[q].y, y[q].z, y[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[2 * e] = fmaf(w[q], bf16_bits_to_f32(yw[e] & 0xFFFFu), s[2 * e]);
+                s[2 * e + 1] = fmaf(w[q], bf16_bits_to_f32(yw[e] >> 16), s[2 * e + 1]);
+            }
+        }
     }
     if (a.has_shared) add_row((size_t)a.T * a.topk + t, 1.0f);
     u32x4_t o;
