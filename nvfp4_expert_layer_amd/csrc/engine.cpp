@@ -63,8 +63,9 @@ int resolve_path(const moe_nvfp4_problem& p) {
 
 struct Plan {
     int KS = 1, path = 1, BM = 16, max_tiles = 0, nblk = 0;
+    bool exact = false;  // routing by exact fp64 logits (few tokens), else certified
     size_t rows = 0;  // rows of the expanded (pair + shared) activation space
-    size_t part, xn2, gn2, mlog, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
+    size_t part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
         ntiles, perm, inv, hq, act, Y, total;
 };
 
@@ -101,7 +102,8 @@ int check_problem(const moe_nvfp4_problem* p) {
 void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     const size_t T = p.num_tokens, k = p.top_k, E = p.num_experts, L = p.num_local_experts;
     const size_t d = p.d_model, F = p.d_ff;
-    pl.KS = moe::router_ksplit((int)T, (int)E, (int)d);
+    pl.exact = moe::router_exact((int)T, (int)E, (int)d);
+    pl.KS = pl.exact ? moe::router_exact_ksplit((int)T, (int)E, (int)d) : moe::router_ksplit((int)T, (int)E, (int)d);
     pl.path = resolve_path(p);
     pl.BM = moe::gemm_bm(pl.path, (int)T, (int)k, (int)E);
     const size_t bm = pl.BM;
@@ -110,11 +112,9 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.rows = T * k + (p.has_shared ? T : 0);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
-    pl.part = take((size_t)pl.KS * T * E * 4);
-    pl.xn2 = take((size_t)pl.KS * T * 8);
-    pl.gn2 = take((size_t)pl.KS * E * 8);
-    const bool micro = T >= 1 && T <= (size_t)moe::router_micro_tokens();
-    pl.mlog = take(micro ? T * E * 8 : 0);              // fp64 logits of the few-token routing
+    pl.part = take((size_t)pl.KS * T * E * (pl.exact ? 8 : 4));
+    pl.xn2 = take(pl.exact ? 0 : (size_t)pl.KS * T * 8);
+    pl.gn2 = take(pl.exact ? 0 : (size_t)pl.KS * E * 8);
     pl.topk_ids = take(T * k * 4);
     pl.topk_w = take(T * k * 4);
     pl.local_ids = take(T * k * 4);
@@ -193,6 +193,7 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     r.T = p.num_tokens; r.E = p.num_experts; r.d = p.d_model; r.KS = pl.KS; r.topk = p.top_k;
     r.offset = p.local_expert_offset; r.L = p.num_local_experts;
     r.part = at<float>(ws, pl.part); r.xn2 = at<double>(ws, pl.xn2); r.gn2 = at<double>(ws, pl.gn2);
+    r.xpart = at<double>(ws, pl.part);
     r.topk_ids = ids_out ? ids_out : at<int32_t>(ws, pl.topk_ids);
     r.topk_w = w_out ? w_out : at<float>(ws, pl.topk_w);
     r.local_ids = at<int32_t>(ws, pl.local_ids);
@@ -204,9 +205,7 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     q.offsets = offsets_out ? offsets_out : at<int32_t>(ws, pl.offsets);
     q.tiles = at<int4>(ws, pl.tiles); q.ntiles = at<int32_t>(ws, pl.ntiles);
     q.perm = perm_out ? perm_out : at<int32_t>(ws, pl.perm); q.inv = at<int32_t>(ws, pl.inv);
-    if (p.num_tokens >= 1 && p.num_tokens <= moe::router_micro_tokens())
-        return hip_status(moe::launch_route_micro(r, q, at<double>(ws, pl.mlog), s), "routing launch");
-    int st = hip_status(moe::launch_router(r, s), "router launch");
+    int st = hip_status(pl.exact ? moe::launch_route_exact(r, s) : moe::launch_router(r, s), "router launch");
     if (st) return st;
     return hip_status(moe::launch_permute(q, s), "permutation launch");
 }

@@ -18,7 +18,8 @@ struct RouterArgs {
     const uint16_t* X;            // bf16 [T][d]
     const uint16_t* G;            // bf16 [E][d]
     int T, E, d, KS, topk, offset, L;
-    float* part;                  // [KS][T][E]
+    float* part;                  // [KS][T][E]  (certified routing)
+    double* xpart;                // [KS][T][E]  (exact routing)
     double* xn2;                  // [KS][T]
     double* gn2;                  // [KS][E]
     int32_t* topk_ids;            // [T][k]
@@ -74,8 +75,9 @@ struct CombineArgs {
 
 int router_ksplit(int T, int E, int d);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
-int router_micro_tokens();                        // T up to which routing takes the two-launch path
-hipError_t launch_route_micro(const RouterArgs& a, const PermArgs& q, double* logits, hipStream_t s);
+bool router_exact(int T, int E, int d);           // exact fp64 logits for this batch
+int router_exact_ksplit(int T, int E, int d);
+hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int R, int C, float g, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);

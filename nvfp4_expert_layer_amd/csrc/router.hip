@@ -622,7 +622,7 @@ __device__ void perm_small_body(const int32_t* __restrict__ local_ids, int T, in
     if (tid < T)
         for (int j = 0; j < topk; ++j) {
             const int lam = local_ids[(size_t)tid * topk + j];
-            if (lam >= 0) atomicOr(&masks[lam * W + (tid >> 5)], 1u << (tid & 31));
+            if ((unsigned)lam < (unsigned)L) atomicOr(&masks[lam * W + (tid >> 5)], 1u << (tid & 31));
         }
     __syncthreads();
     int c = 0;
@@ -634,7 +634,7 @@ __device__ void perm_small_body(const int32_t* __restrict__ local_ids, int T, in
         const int t = p / topk;
         const int lam = local_ids[p];
         int pos = -1;
-        if (lam >= 0) {
+        if ((unsigned)lam < (unsigned)L) {
             int r = 0;
             for (int w = 0; w < (t >> 5); ++w) r += __popc(masks[lam * W + w]);
             r += __popc(masks[lam * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
@@ -655,125 +655,168 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Few tokens (T <= kMicroTokens): routing in two launches.  With so few rows
-// the logits are computed exactly in fp64 (bf16 x bf16 products are exact;
-// one wave sums an expert's products for every token in a fixed order), so
-// the selection needs no error bounds or candidate re-scoring; the second
-// kernel selects the top-k of each token (a wave per token), forms the
-// weights and the shard filter, and builds the permutation in the same
-// workgroup.
+// Few tokens: exact routing in two launches.  With few rows the logits are
+// computed in fp64 outright, so the selection needs no error bounds and no
+// candidate re-scoring.  bf16 x bf16 products are exact in fp64; they are
+// summed on the fp64 matrix cores (v_mfma_f64_16x16x4_f64), whose order is
+// fixed by the hardware, then over the four waves of a workgroup in wave
+// order, then over the K slices in slice order: the logits are deterministic
+// fp64 sums of the exact products.
+//
+// v_mfma_f64_16x16x4_f64: lane l supplies A[l%16][l/16] and B[l/16][l%16]; item
+// r of the result is D[l/16 + 4r][l%16] (checked on the hardware).  A = 16 gate
+// rows, B = 16 token rows.  The reduction index is a free permutation: lane
+// group q = l/16 loads 8 consecutive elements k0 + 8q .. +8 of its row and
+// feeds element j to MFMA j, so one 16-byte load per lane and row serves
+// eight MFMAs over 32 elements of K.
 // ---------------------------------------------------------------------------
-constexpr int kMicroTokens = 16;
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kXMaxTG = 4;          // token groups of 16 per workgroup (64 tokens)
+constexpr int kXTokens = 128;       // exact routing up to this many tokens
+constexpr double kXMaxMacs = 536870912.0;   // ... and up to T E d = 2^29 products
 
-// logits [T][E] fp64: workgroup e takes expert e; thread i multiplies the
-// 8-element pieces i, i + 256, ... of the gate row and of every token's row
-// (all of a piece's loads issued together), a fixed xor butterfly sums each
-// wave, and the four wave sums are added in wave order.
-__global__ __launch_bounds__(256) void router_micro_logits_kernel(const uint16_t* __restrict__ X,
-                                                                  const uint16_t* __restrict__ G, int T, int E,
-                                                                  int d, double* __restrict__ logits) {
-    __shared__ double s_part[4][kMicroTokens];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e = blockIdx.x;
-    const uint16_t* g = G + (size_t)e * d;
-    double acc[kMicroTokens];
+__device__ __forceinline__ double bf16_elem_f64(const u32x4_t& v, int j) {
+    const uint32_t w = v[j >> 1];
+    return (double)__uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// partial logits [ks][T][E] over K slice ks: workgroup = 16 experts x 16 TG
+// tokens; wave w takes the w-th quarter of the slice.
+template <int TG>
+__global__ __launch_bounds__(256) void router_exact_logits_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, int T, int E, int d, int kslice,
+    double* __restrict__ part) {
+    __shared__ f64x4_t s_red[3][TG][64];
+    __shared__ double s_out[16 * TG][17];                    // [token][expert], padded
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int e0 = blockIdx.x * 16, ks = blockIdx.y, t0 = blockIdx.z * (16 * TG);
+    const int i = lane & 15, q = lane >> 4;
+    // rows past E or T repeat the last row; their results are not stored
+    const uint16_t* gp = G + (size_t)min(e0 + i, E - 1) * d + 8 * q;
+    const uint16_t* xp[TG];
 #pragma unroll
-    for (int t = 0; t < kMicroTokens; ++t) acc[t] = 0.0;
-    for (int c = tid * 8; c < d; c += 256 * 8) {
-        const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(g + c);
-        u32x4_t xv[kMicroTokens];
+    for (int tg = 0; tg < TG; ++tg) xp[tg] = X + (size_t)min(t0 + 16 * tg + i, T - 1) * d + 8 * q;
+    const int wlen = kslice / 4;                             // a multiple of 32
+    const int kb = ks * kslice + wave * wlen, ke = min(kb + wlen, d);
+    f64x4_t acc[TG];
 #pragma unroll
-        for (int t = 0; t < kMicroTokens; ++t)
-            if (t < T) xv[t] = *reinterpret_cast<const u32x4_t*>(X + (size_t)t * d + c);
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-        double gf[8];
+    for (int tg = 0; tg < TG; ++tg) acc[tg] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+    u32x4_t ga{0u, 0u, 0u, 0u}, xb[TG];
+    if (kb < ke) {
+        ga = *reinterpret_cast<const u32x4_t*>(gp + kb);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            gf[2 * q] = (double)__uint_as_float(gw[q] << 16);
-            gf[2 * q + 1] = (double)__uint_as_float(gw[q] & 0xFFFF0000u);
+        for (int tg = 0; tg < TG; ++tg) xb[tg] = *reinterpret_cast<const u32x4_t*>(xp[tg] + kb);
+    }
+    for (int k0 = kb; k0 < ke; k0 += 32) {
+        const u32x4_t gc = ga;
+        u32x4_t xc[TG];
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) xc[tg] = xb[tg];
+        if (k0 + 32 < ke) {                                  // next step's loads go out first
+            ga = *reinterpret_cast<const u32x4_t*>(gp + k0 + 32);
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) xb[tg] = *reinterpret_cast<const u32x4_t*>(xp[tg] + k0 + 32);
         }
 #pragma unroll
-        for (int t = 0; t < kMicroTokens; ++t) {
-            if (t < T) {
-                const uint32_t xw[4] = {xv[t].x, xv[t].y, xv[t].z, xv[t].w};
+        for (int j = 0; j < 8; ++j) {
+            const double av = bf16_elem_f64(gc, j);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[t] = fma((double)__uint_as_float(xw[q] << 16), gf[2 * q], acc[t]);
-                    acc[t] = fma((double)__uint_as_float(xw[q] & 0xFFFF0000u), gf[2 * q + 1], acc[t]);
-                }
-            }
+            for (int tg = 0; tg < TG; ++tg)
+                acc[tg] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bf16_elem_f64(xc[tg], j), acc[tg], 0, 0, 0);
         }
     }
+    if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < kMicroTokens; ++t) {
-        if (t < T) {
-            const double v = wave_sum_f64(acc[t]);
-            if (lane == 0) s_part[wave][t] = v;
+        for (int tg = 0; tg < TG; ++tg) s_red[wave - 1][tg][lane] = acc[tg];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg) {
+            f64x4_t v = acc[tg];                             // the four waves' sums in wave order
+            v += s_red[0][tg][lane];
+            v += s_red[1][tg][lane];
+            v += s_red[2][tg][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_out[16 * tg + i][q + 4 * r] = v[r];
         }
     }
     __syncthreads();
-    if (tid < T) logits[(size_t)tid * E + e] = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+    // each token's 16 experts are 128 contiguous bytes of the partial row
+    for (int c = tid; c < 16 * TG * 16; c += 256) {
+        const int tt = c >> 4, ee = c & 15;
+        if (t0 + tt < T && e0 + ee < E) part[((size_t)ks * T + t0 + tt) * E + e0 + ee] = s_out[tt][ee];
+    }
 }
 
-// top-k per token (wave t < T; experts e = lane + 64 s, s < EPL): k rounds of
-// (wave max of the score, then the lowest id holding it); softmax over the k
-// in fp64; then the permutation of all T * k pairs by the whole workgroup.
+// Order-preserving 64-bit key of an fp64 value (+0 and -0 share a key: the
+// value is canonicalised first); 0 is below every key.
+__device__ __forceinline__ uint64_t f64_key(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// top-k of token t: logits = the K-slice partials added in slice order; wave 0
+// takes k rounds of (the largest remaining key, then the lowest id holding it);
+// softmax over the k in fp64.  Experts e = lane + 64 s, s < EPL.
 template <int EPL>
-__global__ __launch_bounds__(1024) void router_micro_select_kernel(
-    const double* __restrict__ logits, int T, int E, int topk, int offset, int L, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w, int32_t* __restrict__ local_ids, int has_shared, int BM,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
-    int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-    extern __shared__ uint32_t masks[];                  // [L][kPermBlock/32]
-    __shared__ int32_t s_id[kMicroTokens][32];
-    __shared__ double s_sc[kMicroTokens][32];
-    __shared__ int32_t s_lam[kMicroTokens * 32];        // local ids, [T][k]
-    const int lane = threadIdx.x & 63, t = threadIdx.x >> 6;
-    if (t < T) {
-        double v[EPL];
+__global__ __launch_bounds__(1024) void router_exact_select_kernel(
+    const double* __restrict__ part, int T, int E, int KS, int topk, int offset, int L,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ local_ids) {
+    __shared__ double s_val[kMaxExperts];
+    __shared__ int32_t s_id[32];
+    __shared__ double s_sc[32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x;
+    if (tid < E) {
+        double pv[kMaxKS];
 #pragma unroll
-        for (int s = 0; s < EPL; ++s) {
-            const int e = lane + 64 * s;
-            v[s] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
-        }
-        for (int r = 0; r < topk; ++r) {
-            // this lane's best (largest score; the lowest id among equal scores)
-            double m = v[0];
-            int me = lane;
+        for (int sl = 0; sl < kMaxKS; ++sl) pv[sl] = part[((size_t)min(sl, KS - 1) * T + t) * E + tid];
+        double v = pv[0];
 #pragma unroll
-            for (int s = 1; s < EPL; ++s)
-                if (v[s] > m) { m = v[s]; me = lane + 64 * s; }
-            double M = m;
+        for (int sl = 1; sl < kMaxKS; ++sl)
+            if (sl < KS) v += pv[sl];
+        s_val[tid] = v;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    uint64_t key[EPL];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
-            int id = (m == M && me < E) ? me : 0x7FFFFFFF;
+    for (int sl = 0; sl < EPL; ++sl) {
+        const int e = lane + 64 * sl;
+        key[sl] = e < E ? f64_key(s_val[e]) : 0ull;
+    }
+    for (int r = 0; r < topk; ++r) {
+        uint64_t m = 0;
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) id = min(id, __shfl_xor(id, o, 64));
-            if ((id & 63) == lane) {
+        for (int sl = 0; sl < EPL; ++sl) m = key[sl] > m ? key[sl] : m;
+        const uint64_t M = wave_max_u64(m);
+        uint32_t c = 0;                                  // 0xFFFFFFFF - id: the max is the lowest id
 #pragma unroll
-                for (int s = 0; s < EPL; ++s)
-                    if (lane + 64 * s == id) v[s] = -INFINITY;
-            }
-            if (lane == 0) {
-                s_id[t][r] = id;
-                s_sc[t][r] = M;
-            }
-        }
-        __builtin_amdgcn_wave_barrier();                 // (a wave's LDS accesses complete in order)
-        const double my = lane < topk ? s_sc[t][lane] : 0.0;
-        const double z = lane < topk ? exp(my - s_sc[t][0]) : 0.0;
-        const double zs = wave_sum_f64(z);
-        if (lane < topk) {
-            const int my_id = s_id[t][lane];
-            const size_t o = (size_t)t * topk + lane;
-            topk_ids[o] = my_id;
-            topk_w[o] = (float)(z / zs);
-            const int lam = my_id - offset;
-            local_ids[o] = s_lam[o] = (lam >= 0 && lam < L) ? lam : -1;
+        for (int sl = EPL - 1; sl >= 0; --sl)
+            if (key[sl] == M) c = 0xFFFFFFFFu - (uint32_t)(lane + 64 * sl);
+        const int id = (int)(0xFFFFFFFFu - wave_max_u32(c));
+#pragma unroll
+        for (int sl = 0; sl < EPL; ++sl)
+            if (lane + 64 * sl == id) key[sl] = 0;
+        if (lane == 0) {
+            s_id[r] = id;
+            s_sc[r] = s_val[id];
         }
     }
-    __syncthreads();                                     // every token's local ids are in LDS
-    perm_small_body(s_lam, T, topk, L, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, perm, inv, masks);
+    __builtin_amdgcn_wave_barrier();                     // (a wave's LDS accesses complete in order)
+    const double my = lane < topk ? s_sc[lane] : 0.0;
+    const double z = lane < topk ? exp(my - s_sc[0]) : 0.0;
+    const double zs = wave_sum_f64(z);
+    if (lane < topk) {
+        const int my_id = s_id[lane];
+        const size_t o = (size_t)t * topk + lane;
+        topk_ids[o] = my_id;
+        topk_w[o] = (float)(z / zs);
+        const int lam = my_id - offset;
+        local_ids[o] = (lam >= 0 && lam < L) ? lam : -1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -838,19 +881,40 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-int router_micro_tokens() { return kMicroTokens; }
+bool router_exact(int T, int E, int d) {
+    return T >= 1 && T <= kXTokens && (double)T * E * d <= kXMaxMacs;
+}
 
-hipError_t launch_route_micro(const RouterArgs& a, const PermArgs& q, double* logits, hipStream_t s) {
-    if (a.T < 1 || a.T > kMicroTokens) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(router_micro_logits_kernel, dim3(a.E), dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, logits);
-    const size_t lds = (size_t)q.L * (kPermBlock / 32) * sizeof(uint32_t);
-    auto k = a.E <= 128 ? router_micro_select_kernel<2>
-             : a.E <= 320 ? router_micro_select_kernel<5>
-             : a.E <= 512 ? router_micro_select_kernel<8>
-                          : router_micro_select_kernel<kMaxExperts / 64>;
-    hipLaunchKernelGGL(k, dim3(1), dim3(1024), lds, s, logits, a.T, a.E, a.topk, a.offset, a.L, a.topk_ids,
-                       a.topk_w, a.local_ids, q.has_shared, q.BM, q.counts, q.offsets, q.tiles, q.ntiles,
-                       q.max_tiles, q.perm, q.inv);
+// K slices of the exact logits: enough workgroups for the chip (about 320),
+// at most kMaxKS, each slice a multiple of 128 elements (32 per wave).
+int router_exact_ksplit(int T, int E, int d) {
+    const int base = ((E + 15) / 16) * ((T + 16 * kXMaxTG - 1) / (16 * kXMaxTG));
+    int ks = (320 + base - 1) / base;
+    if (ks > kMaxKS) ks = kMaxKS;
+    if (ks > d / 128) ks = d / 128;
+    return ks < 1 ? 1 : ks;
+}
+
+hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
+    if (!router_exact(a.T, a.E, a.d) || a.KS < 1 || a.KS > kMaxKS) return hipErrorInvalidValue;
+    const int kslice = ((a.d + a.KS - 1) / a.KS + 127) / 128 * 128;
+    const int tg = a.T <= 16 ? 1 : (a.T <= 32 ? 2 : kXMaxTG);
+    const dim3 g1((a.E + 15) / 16, a.KS, (a.T + 16 * tg - 1) / (16 * tg));
+    if (tg == 1)
+        hipLaunchKernelGGL(router_exact_logits_kernel<1>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
+                           a.xpart);
+    else if (tg == 2)
+        hipLaunchKernelGGL(router_exact_logits_kernel<2>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
+                           a.xpart);
+    else
+        hipLaunchKernelGGL(router_exact_logits_kernel<kXMaxTG>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
+                           a.xpart);
+    auto k = a.E <= 128 ? router_exact_select_kernel<2>
+             : a.E <= 320 ? router_exact_select_kernel<5>
+             : a.E <= 512 ? router_exact_select_kernel<8>
+                          : router_exact_select_kernel<kMaxExperts / 64>;
+    hipLaunchKernelGGL(k, dim3(a.T), dim3(1024), 0, s, a.xpart, a.T, a.E, a.KS, a.topk, a.offset, a.L, a.topk_ids,
+                       a.topk_w, a.local_ids);
     return hipGetLastError();
 }
 

@@ -119,10 +119,11 @@ def test_route_empty_batch():
     assert not counts.any().item() and not offsets.any().item()
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 16, 17])
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 17, 33, 64, 65, 128, 129])
 def test_route_few_tokens_both_sides_of_the_exact_fp64_path(T):
-    """Up to 16 tokens the logits are computed exactly in fp64 (no bounds, no
-    re-scoring); 17 tokens take the certified bf16-MFMA path."""
+    """Up to 128 tokens the logits are computed exactly in fp64 on the matrix
+    cores (no bounds, no re-scoring; token tiles of 16, 32 and 64 rows, full and
+    ragged); 129 tokens take the certified bf16-MFMA path."""
     require_gpu()
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     log(f"route few tokens T={T}")
