@@ -50,15 +50,16 @@ KERNEL_SOURCES = {"decode": ["decode.hip", "device_common.h", "kernels.h"],
 
 def kernel_source_hash(path):
     """Hash of what the path's GEMM kernels are built from: their source file,
-    the device helpers, and the argument structs they receive (kernels.h's
-    host-side declarations are left out: adding a launcher changes no kernel)."""
+    the device helpers, and the two argument structs they receive (the rest of
+    kernels.h -- other kernels' structs, host-side declarations -- is left out:
+    it changes no GEMM kernel)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[path]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             text = fh.read()
         t = text.decode()
         if f == "kernels.h":
-            t = t[t.index("struct ExpertWeights"):t.index("struct CombineArgs")]
+            t = "".join(re.findall(r"struct (?:ExpertWeights|GemmArgs) \{.*?\n\};", t, flags=re.S))
         t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)          # comments do not change a kernel
         t = re.sub(r"//[^\n]*", "", t)
         h.update(t.encode())

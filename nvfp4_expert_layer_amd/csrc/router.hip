@@ -74,9 +74,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
             *reinterpret_cast<u32x4_t*>(&gs[b][r][cc]) = vg[c];
         }
     };
-    // squared norms: thread tid < 64 -> token row t0+tid; 64..127 -> expert row e0+tid-64
-    double nrm = 0.0;
-    const bool want = tid < 64 ? (blockIdx.y == 0) : (tid < 128 && blockIdx.x == 0);
+    // squared norms (token rows in the first expert tile, expert rows in the
+    // first token tile): four threads per row, each a quarter of every chunk in
+    // two chains; the quarters are added by a fixed butterfly at the end
+    double nx[2] = {0.0, 0.0}, ng[2] = {0.0, 0.0};
+    const bool want_x = blockIdx.y == 0, want_g = blockIdx.x == 0;
+    const int nrow = tid >> 2, nq = (tid & 3) * 16;
     if (kbeg < kend) {
         load(kbeg);
         store(0);
@@ -86,13 +89,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     for (int k0 = kbeg; k0 < kend; k0 += kR1BK) {
         const bool more = k0 + kR1BK < kend;
         if (more) load(k0 + kR1BK);
-        if (want) {
-            const uint16_t* row = tid < 64 ? xs[b][tid] : gs[b][tid - 64];
-            for (int j = 0; j < kR1BK; ++j) {
-                const double v = (double)bf16_bits_to_f32(row[j]);
-                nrm = fma(v, v, nrm);
+        auto sq16 = [&](const uint16_t* row, double (&acc)[2]) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(row);
+            const u32x4_t c = *reinterpret_cast<const u32x4_t*>(row + 8);
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const double lo = (double)__uint_as_float(w[q] << 16), hi = (double)__uint_as_float(w[q] & 0xFFFF0000u);
+                acc[q & 1] = fma(lo, lo, acc[q & 1]);
+                acc[q & 1] = fma(hi, hi, acc[q & 1]);
             }
-        }
+        };
+        if (want_x) sq16(&xs[b][nrow][nq], nx);
+        if (want_g) sq16(&gs[b][nrow][nq], ng);
 #pragma unroll
         for (int kk = 0; kk < kR1BK; kk += 32) {
             bf16x8_t a[2], bb[2];
@@ -123,8 +132,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
                 const int e = e0 + wn * 32 + j * 16 + (lane & 15);
                 if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][r];
             }
-    if (tid < 64 && blockIdx.y == 0 && t0 + tid < T) xn2[(size_t)ks * T + t0 + tid] = nrm;
-    if (tid >= 64 && tid < 128 && blockIdx.x == 0 && e0 + tid - 64 < E) gn2[(size_t)ks * E + e0 + tid - 64] = nrm;
+    double sx = nx[0] + nx[1], sg = ng[0] + ng[1];
+    sx += __shfl_xor(sx, 1, 64);
+    sx += __shfl_xor(sx, 2, 64);
+    sg += __shfl_xor(sg, 1, 64);
+    sg += __shfl_xor(sg, 2, 64);
+    if ((tid & 3) == 0) {
+        if (want_x && t0 + nrow < T) xn2[(size_t)ks * T + t0 + nrow] = sx;
+        if (want_g && e0 + nrow < E) gn2[(size_t)ks * E + e0 + nrow] = sg;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -384,8 +400,43 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
     const double n = (double)(d + KS);
     const double gamma = n * u / (1.0 - n * u) * (1.0 + 1e-6);
     const double tiny = (double)d * 1.1754943508222875e-38;
+    // the split-K partials are added in slice order; four slices' loads (for
+    // every slot) go out together
     double xs2 = 0.0;
-    for (int s = 0; s < KS; ++s) xs2 += xn2[(size_t)s * T + t];
+    float lh[kWSlots];
+    double gs2[kWSlots];
+#pragma unroll
+    for (int sl = 0; sl < kWSlots; ++sl) {
+        lh[sl] = 0.f;
+        gs2[sl] = 0.0;
+    }
+    const int ec = E - 1;
+    for (int s0 = 0; s0 < KS; s0 += 4) {
+        double xv[4], gv[4][kWSlots];
+        float pv[4][kWSlots];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = min(s0 + j, KS - 1);
+            xv[j] = xn2[(size_t)s * T + t];
+#pragma unroll
+            for (int sl = 0; sl < kWSlots; ++sl) {
+                const int e = min(lane + 64 * sl, ec);
+                pv[j][sl] = part[((size_t)s * T + t) * E + e];
+                gv[j][sl] = gn2[(size_t)s * E + e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (s0 + j < KS) {
+                xs2 += xv[j];
+#pragma unroll
+                for (int sl = 0; sl < kWSlots; ++sl) {
+                    lh[sl] += pv[j][sl];
+                    gs2[sl] += gv[j][sl];
+                }
+            }
+        }
+    }
     const double xnorm = sqrt(xs2) * (1.0 + 1e-12);
     double hi[kWSlots];
     uint64_t key[kWSlots];
@@ -395,15 +446,9 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
         key[sl] = 0;                                     // below every valid key
         const int e = lane + 64 * sl;
         if (e < E) {
-            float lh = 0.f;
-            double gs2 = 0.0;
-            for (int s = 0; s < KS; ++s) {
-                lh += part[((size_t)s * T + t) * E + e];
-                gs2 += gn2[(size_t)s * E + e];
-            }
-            const double beta = gamma * xnorm * (sqrt(gs2) * (1.0 + 1e-12)) + tiny;
-            hi[sl] = (double)lh + beta;
-            key[sl] = rank_key((double)lh - beta, e);
+            const double beta = gamma * xnorm * (sqrt(gs2[sl]) * (1.0 + 1e-12)) + tiny;
+            hi[sl] = (double)lh[sl] + beta;
+            key[sl] = rank_key((double)lh[sl] - beta, e);
         }
     }
 
@@ -431,43 +476,62 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 
-    // ---- fp64 re-scoring ----
+    // ---- fp64 re-scoring: groups of up to kWGroup candidates; the K loop is
+    // software-pipelined (the next 512-element chunk's loads go out before
+    // this chunk is multiplied); a short last group skips its empty slots ----
     const uint16_t* xrow = X + (size_t)t * d;
     for (int g0 = 0; g0 < nc; g0 += kWGroup) {
         const int ng = min(kWGroup, nc - g0);
-        int ids[kWGroup];
+        const uint16_t* grow[kWGroup];
 #pragma unroll
-        for (int c = 0; c < kWGroup; ++c) ids[c] = cid[g0 + (c < ng ? c : 0)];
+        for (int c = 0; c < kWGroup; ++c) grow[c] = G + (size_t)cid[g0 + (c < ng ? c : 0)] * d;
         double acc[kWGroup];
 #pragma unroll
         for (int c = 0; c < kWGroup; ++c) acc[c] = 0.0;
-        for (int k0 = lane * 8; k0 < d; k0 += 512) {
-            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(xrow + k0);
+        int k0 = lane * 8;
+        u32x4_t xv{0u, 0u, 0u, 0u}, gv[kWGroup];
+        if (k0 < d) {
+            xv = *reinterpret_cast<const u32x4_t*>(xrow + k0);
+#pragma unroll
+            for (int c = 0; c < kWGroup; ++c)
+                if (c < ng) gv[c] = *reinterpret_cast<const u32x4_t*>(grow[c] + k0);
+        }
+        for (; k0 < d; k0 += 512) {
+            const u32x4_t xc = xv;
+            u32x4_t gc[kWGroup];
+#pragma unroll
+            for (int c = 0; c < kWGroup; ++c) gc[c] = gv[c];
+            if (k0 + 512 < d) {
+                xv = *reinterpret_cast<const u32x4_t*>(xrow + k0 + 512);
+#pragma unroll
+                for (int c = 0; c < kWGroup; ++c)
+                    if (c < ng) gv[c] = *reinterpret_cast<const u32x4_t*>(grow[c] + k0 + 512);
+            }
             double xd[8];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            const uint32_t xw[4] = {xc.x, xc.y, xc.z, xc.w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 xd[2 * q] = (double)__uint_as_float(xw[q] << 16);
                 xd[2 * q + 1] = (double)__uint_as_float(xw[q] & 0xFFFF0000u);
             }
-            u32x4_t gv[kWGroup];
-#pragma unroll
-            for (int c = 0; c < kWGroup; ++c)
-                gv[c] = *reinterpret_cast<const u32x4_t*>(G + (size_t)ids[c] * d + k0);
 #pragma unroll
             for (int c = 0; c < kWGroup; ++c) {
-                const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+                if (c < ng) {
+                    const uint32_t gw[4] = {gc[c].x, gc[c].y, gc[c].z, gc[c].w};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[c] = fma(xd[2 * q], (double)__uint_as_float(gw[q] << 16), acc[c]);
-                    acc[c] = fma(xd[2 * q + 1], (double)__uint_as_float(gw[q] & 0xFFFF0000u), acc[c]);
+                    for (int q = 0; q < 4; ++q) {
+                        acc[c] = fma(xd[2 * q], (double)__uint_as_float(gw[q] << 16), acc[c]);
+                        acc[c] = fma(xd[2 * q + 1], (double)__uint_as_float(gw[q] & 0xFFFF0000u), acc[c]);
+                    }
                 }
             }
         }
 #pragma unroll
         for (int c = 0; c < kWGroup; ++c) {
-            const double sc = wave_sum_f64(acc[c]);
-            if (c < ng && lane == 0) csc[g0 + c] = sc;
+            if (c < ng) {
+                const double sc = wave_sum_f64(acc[c]);
+                if (lane == 0) csc[g0 + c] = sc;
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(0);
