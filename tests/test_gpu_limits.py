@@ -3,9 +3,10 @@
     d = 128: the weight-streaming kernels then stage the token rows in
     chunks (the whole K no longer fits in LDS), and the tiled kernels run 256
     K steps and the widest column grids;
-  * E = 1024 experts with top-32 (the largest routing), through the few-token
-    and the many-token selection kernels and a full layer over all 1024 local
-    experts (every permutation counter at its widest).
+  * E = 1024 experts with top-32 (the largest routing), through the exact
+    (few-token) and both certified selection kernels, at d = 256 and at the
+    widest model d = 16384, and a full layer over all 1024 local experts (every
+    permutation counter at its widest).
 Full outputs within 1e-2 (W4A16) / 3e-2 (W4A4); routing ids, counts, offsets
 and permutation bit-exact."""
 import pytest
@@ -60,6 +61,20 @@ def test_route_1024_experts_top32(T):
     amb, diff, P = _check(x, G, w, 100, 900, True)
     log(f"  ambiguous {amb}, differing {diff}, local pairs {P}")
     assert P > 0
+
+
+@pytest.mark.parametrize("T", [24, 40])
+def test_route_1024_experts_widest_model(T):
+    """E = 1024, top-32, d = 16384: 24 tokens take the exact fp64 logits with
+    five ragged K slices (T E d <= 2^29), 40 tokens the certified path."""
+    require_gpu()
+    w = workloads.replace(MANY_E, T=T, d=16384, gate_std=0.02)
+    log(f"route E=1024 k=32 d=16384 T={T}")
+    x = workloads.gen_hidden(w, "cuda")
+    G = workloads.gen_gate(w, "cuda")
+    amb, diff, P = _check(x, G, w, 0, 1024, True)
+    log(f"  ambiguous {amb}, differing {diff}, local pairs {P}")
+    assert P == T * 32
 
 
 @pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
