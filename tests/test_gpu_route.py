@@ -136,3 +136,19 @@ def test_route_few_tokens_both_sides_of_the_exact_fp64_path(T):
         ids, wts, *_ = _route_gpu(x, G.t().contiguous(), w, w.offset, w.L, w.has_shared)
         assert ids[1].tolist() == list(range(w.k))
         assert np.allclose(wts[1], 1.0 / w.k, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("T,L", [(256, 160), (257, 160), (512, 160), (513, 160), (384, 1024), (385, 1024)])
+def test_route_permutation_one_workgroup_and_blocked(T, L):
+    """Up to 512 tokens (bitmask of L x ceil(T/32) words within 48 KB) one
+    workgroup builds the whole permutation; beyond, per-256-token blocks, a scan
+    and a scatter.  Both sides of each bound, against the oracle."""
+    require_gpu()
+    E = max(320, L)
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T, E=E, L=L, offset=0)
+    log(f"route permutation T={T} E={E} L={L}")
+    x = workloads.gen_hidden(w, "cuda")
+    G = workloads.gen_gate(w, "cuda")
+    amb, diff, P = _check(x, G, w, 0, L, True)
+    log(f"  ambiguous {amb}, differing {diff}, local pairs P={P}")
+    assert P > 0
