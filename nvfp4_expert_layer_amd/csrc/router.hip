@@ -664,10 +664,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
     // per-expert scan over blocks (L <= 1024: one thread per expert)
     int total = 0;
     if (tid < L) {
-        for (int b = 0; b < nblk; ++b) {
-            int c = block_counts[(size_t)b * L + tid];
-            block_counts[(size_t)b * L + tid] = total;
-            total += c;
+        // eight blocks' counts are loaded together, then scanned in block order
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = block_counts[(size_t)min(b0 + j, nblk - 1) * L + tid];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (b0 + j < nblk) {
+                    block_counts[(size_t)(b0 + j) * L + tid] = total;
+                    total += c[j];
+                }
+            }
         }
     }
     scan_and_emit_tiles(total, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, nullptr);
