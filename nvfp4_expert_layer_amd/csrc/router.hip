@@ -751,6 +751,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
 // ---------------------------------------------------------------------------
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 constexpr int kXMaxTG = 4;          // token groups of 16 per workgroup (64 tokens)
+constexpr int kXWaves = 8;          // waves per workgroup, each a share of the K slice
 constexpr int kXTokens = 128;       // exact routing up to this many tokens
 constexpr double kXMaxMacs = 536870912.0;   // ... and up to T E d = 2^29 products
 
@@ -761,11 +762,11 @@ __device__ __forceinline__ double bf16_elem_f64(const u32x4_t& v, int j) {
 
 // partial logits [ks][T][E] over K slice ks: workgroup = 16 experts x 16 TG
 // tokens; wave w takes the w-th quarter of the slice.
-template <int TG>
-__global__ __launch_bounds__(256) void router_exact_logits_kernel(
+template <int TG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void router_exact_logits_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, int T, int E, int d, int kslice,
     double* __restrict__ part) {
-    __shared__ f64x4_t s_red[3][TG][64];
+    __shared__ f64x4_t s_red[WAVES / 2][TG][64];
     __shared__ double s_out[16 * TG][17];                    // [token][expert], padded
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -776,7 +777,7 @@ __global__ __launch_bounds__(256) void router_exact_logits_kernel(
     const uint16_t* xp[TG];
 #pragma unroll
     for (int tg = 0; tg < TG; ++tg) xp[tg] = X + (size_t)min(t0 + 16 * tg + i, T - 1) * d + 8 * q;
-    const int wlen = kslice / 4;                             // a multiple of 32
+    const int wlen = kslice / WAVES;                         // a multiple of 32
     const int kb = ks * kslice + wave * wlen, ke = min(kb + wlen, d);
     f64x4_t acc[TG];
 #pragma unroll
@@ -805,25 +806,30 @@ __global__ __launch_bounds__(256) void router_exact_logits_kernel(
                 acc[tg] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bf16_elem_f64(xc[tg], j), acc[tg], 0, 0, 0);
         }
     }
-    if (wave > 0) {
+    // the waves' sums meet in a fixed pairwise tree: at each level the upper
+    // half of the remaining waves hands its sums to the lower half
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) s_red[wave - 1][tg][lane] = acc[tg];
+    for (int h = WAVES / 2; h >= 1; h >>= 1) {
+        if (wave >= h && wave < 2 * h) {
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) s_red[wave - h][tg][lane] = acc[tg];
+        }
+        __syncthreads();
+        if (wave < h) {
+#pragma unroll
+            for (int tg = 0; tg < TG; ++tg) acc[tg] += s_red[wave][tg][lane];
+        }
+        __syncthreads();
     }
-    __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int tg = 0; tg < TG; ++tg) {
-            f64x4_t v = acc[tg];                             // the four waves' sums in wave order
-            v += s_red[0][tg][lane];
-            v += s_red[1][tg][lane];
-            v += s_red[2][tg][lane];
+        for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) s_out[16 * tg + i][q + 4 * r] = v[r];
-        }
+            for (int r = 0; r < 4; ++r) s_out[16 * tg + i][q + 4 * r] = acc[tg][r];
     }
     __syncthreads();
     // each token's 16 experts are 128 contiguous bytes of the partial row
-    for (int c = tid; c < 16 * TG * 16; c += 256) {
+    for (int c = tid; c < 16 * TG * 16; c += 64 * WAVES) {
         const int tt = c >> 4, ee = c & 15;
         if (t0 + tt < T && e0 + ee < E) part[((size_t)ks * T + t0 + tt) * E + e0 + ee] = s_out[tt][ee];
     }
@@ -965,29 +971,30 @@ bool router_exact(int T, int E, int d) {
 }
 
 // K slices of the exact logits: enough workgroups for the chip (about 320),
-// at most kMaxKS, each slice a multiple of 128 elements (32 per wave).
+// at most kMaxKS, each slice at least 32 elements per wave.
 int router_exact_ksplit(int T, int E, int d) {
     const int base = ((E + 15) / 16) * ((T + 16 * kXMaxTG - 1) / (16 * kXMaxTG));
     int ks = (320 + base - 1) / base;
     if (ks > kMaxKS) ks = kMaxKS;
-    if (ks > d / 128) ks = d / 128;
+    if (ks > d / (32 * kXWaves)) ks = d / (32 * kXWaves);
     return ks < 1 ? 1 : ks;
 }
 
 hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
     if (!router_exact(a.T, a.E, a.d) || a.KS < 1 || a.KS > kMaxKS) return hipErrorInvalidValue;
-    const int kslice = ((a.d + a.KS - 1) / a.KS + 127) / 128 * 128;
+    constexpr int W = kXWaves;
+    const int kslice = ((a.d + a.KS - 1) / a.KS + 32 * W - 1) / (32 * W) * (32 * W);
     const int tg = a.T <= 16 ? 1 : (a.T <= 32 ? 2 : kXMaxTG);
     const dim3 g1((a.E + 15) / 16, a.KS, (a.T + 16 * tg - 1) / (16 * tg));
     if (tg == 1)
-        hipLaunchKernelGGL(router_exact_logits_kernel<1>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
+        hipLaunchKernelGGL((router_exact_logits_kernel<1, W>), g1, dim3(64 * W), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
                            a.xpart);
     else if (tg == 2)
-        hipLaunchKernelGGL(router_exact_logits_kernel<2>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
+        hipLaunchKernelGGL((router_exact_logits_kernel<2, W>), g1, dim3(64 * W), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
                            a.xpart);
     else
-        hipLaunchKernelGGL(router_exact_logits_kernel<kXMaxTG>, g1, dim3(256), 0, s, a.X, a.G, a.T, a.E, a.d, kslice,
-                           a.xpart);
+        hipLaunchKernelGGL((router_exact_logits_kernel<kXMaxTG, W>), g1, dim3(64 * W), 0, s, a.X, a.G, a.T, a.E, a.d,
+                           kslice, a.xpart);
     auto k = a.E <= 128 ? router_exact_select_kernel<2>
              : a.E <= 320 ? router_exact_select_kernel<5>
              : a.E <= 512 ? router_exact_select_kernel<8>
