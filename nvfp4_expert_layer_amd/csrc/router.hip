@@ -7,8 +7,11 @@
 //   logits over ALL experts, top-k by logit (ties -> lower id), weights = softmax
 //   over the k selected logits, local id = id - offset if inside [0, L) else -1.
 //
-// Exactness of the selection.  Logits are first computed with bf16 MFMA (the
-// bf16 x bf16 products are exact in fp32; the accumulation rounds).  For any
+// Exactness of the selection.  Up to 128 tokens the logits are computed in fp64
+// outright on the fp64 matrix cores (bf16 x bf16 products are exact in fp64),
+// and the top-k is taken on them directly.  Beyond that, logits are first
+// computed with bf16 MFMA (the bf16 x bf16 products are exact in fp32; the
+// accumulation rounds) and certified.  For any
 // order of at most n fp32 additions with relative error <= u' each (u' = 2^-23
 // covers round-to-nearest and truncation), |lhat - l| <= gamma_n * sum_k |x_k g_k|
 // <= gamma_n * ||x||_2 * ||g_e||_2 (Cauchy-Schwarz), gamma_n = n u' / (1 - n u'),
@@ -18,11 +21,12 @@
 // top-k.  Every other expert (the candidates) is re-scored in fp64 (exact
 // products, fixed summation order) and the top-k is taken among them.
 //
-// Permutation: pairs grouped by local expert, stable by token.  Per block of 256
-// tokens an LDS bitmask per local expert records which tokens chose it; a pair's
-// rank inside its block is a popcount of the lower bits, so the order is
-// deterministic without sorting.  A single-workgroup scan turns per-block counts
-// into per-block bases, counts, offsets and the GEMM tile table.
+// Permutation: pairs grouped by local expert, stable by token.  An LDS bitmask
+// per local expert records which tokens chose it; a pair's rank is a popcount of
+// the lower bits, so the order is deterministic without sorting.  Up to 512
+// tokens one workgroup does it all; beyond, per block of 256 tokens, and a
+// single-workgroup scan turns per-block counts into per-block bases, counts,
+// offsets and the GEMM tile table.
 #include "device_common.h"
 #include "kernels.h"
 
