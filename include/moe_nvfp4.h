@@ -49,9 +49,11 @@
  * Numerics: code * scale is exact in bf16 (and in f16); the GEMMs run on bf16
  * MFMA (W4A16) or f16 MFMA on the tiled path in W4A4, where both operands are
  * such products, with fp32 accumulation, and apply the fp32 global scale after
- * accumulation.  Routing is
- * exact: bf16-MFMA logits carry a rigorous error bound, and every expert that
- * could be on either side of the top-k boundary is re-scored in fp64.
+ * accumulation.  Routing is exact: up to 128 tokens the logits are fp64 sums of
+ * the exact bf16 x bf16 products (fp64 matrix cores); beyond, bf16-MFMA logits
+ * carry a rigorous error bound, and every expert that could be on either side
+ * of the top-k boundary is re-scored in fp64.  Either way the result is
+ * deterministic.
  *
  * Conventions of every entry point:
  *   - All tensor pointers are DEVICE pointers (HIP), caller-owned, row-major,
