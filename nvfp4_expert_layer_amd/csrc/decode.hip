@@ -29,6 +29,7 @@
 // Layer semantics: the page "Serving Solar Open 2 on DGX Spark", sections "수정
 // 사항 › b12x에서의 Expert Parallelism 구현 추가" and "b12x 버전이 실제 NVFP4
 // 체크포인트를 읽어들이도록 만들기".
+#include <atomic>
 #include <cmath>
 #include "device_common.h"
 #include "kernels.h"
@@ -38,7 +39,7 @@ namespace moe {
 constexpr int kDecWaves = 4;        // waves per workgroup, 16 weight rows each at a time
 constexpr int kChunk = 512;         // K elements per LDS chunk when A is staged in chunks
 constexpr int kAPad = 8;            // bf16 padding per LDS row
-constexpr int kFullALds = 65536;    // largest whole-K A stage (bytes)
+constexpr int kFullALds = 67584;    // largest whole-K A stage (bytes): 8 rows of K = 4096 fit
 
 // LDS bytes of the A stage: whole K, or two chunks.
 __host__ __device__ constexpr int dec_lds_bytes(int rows, int K, bool full) {
@@ -415,9 +416,27 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
     dec_stream<1, TGM, DEPTH, RGS, FULLA, SEG>(s_arow, ntok, F, codes, scales, cstride, sstride, lds, epi);
 }
 
-// Tile height of the decode path: 4 token rows (one group, deep weight prefetch)
-// when experts expect at most ~2 tokens, else 16 rows (four groups).
-int dec_rows(int T, int topk, int E) { return (long long)T * topk <= 2LL * E ? 4 : 16; }
+// Tile height of the decode path: 4 token rows (one group) when experts expect
+// at most ~2 tokens, 8 rows (two groups) up to ~6, else 16 rows (four groups;
+// only when the decode path is forced beyond that).  The 4- and 8-row tiles
+// stage the whole K of their token rows in LDS (up to K = 4096 for 8 rows).
+int dec_rows(int T, int topk, int E) {
+    const long long p = (long long)T * topk;
+    return p <= 2LL * E ? 4 : (p <= 6LL * E ? 8 : 16);
+}
+
+// Launch of a decode kernel with `lds` bytes of dynamic LDS; above 64 KB the
+// kernel's attribute is raised first (once per kernel; a failure is left for
+// hipGetLastError, like a failed launch).
+template <auto Kern>
+static void launch_dec(dim3 grid, int lds, hipStream_t s, const GemmArgs& a) {
+    static std::atomic<int> allowed{65536};
+    if (lds > allowed.load(std::memory_order_relaxed) &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds) ==
+            hipSuccess)
+        allowed.store(lds, std::memory_order_relaxed);
+    hipLaunchKernelGGL(Kern, grid, dim3(64 * kDecWaves), lds, s, a);
+}
 
 constexpr int kG1Depth = 4;         // prefetch ring depth of the small-tile GEMM1
 
@@ -442,28 +461,29 @@ static int g2_row_groups(const GemmArgs& a) {
 template <int MODE, int TGM, int DEPTH, int RG>
 static void launch_g1(const GemmArgs& a, hipStream_t s) {
     const int full = dec_lds_bytes(4 * TGM, a.d, true);
-    const dim3 blk(64 * kDecWaves);
     if (full <= kFullALds && a.F % (32 * RG) == 0) {
         const dim3 grid(a.max_tiles, a.F / (32 * RG));
         if (DEPTH % 4 == 0 && a.d % 1024 == 0)
-            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, (DEPTH % 4 == 0), RG>), grid, blk, full, s, a);
+            launch_dec<dec_gemm1_kernel<MODE, TGM, DEPTH, true, (DEPTH % 4 == 0), RG>>(grid, full, s, a);
         else
-            hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, RG>), grid, blk, full, s, a);
+            launch_dec<dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, RG>>(grid, full, s, a);
     } else if (full <= kFullALds) {
-        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, 1>), dim3(a.max_tiles, a.F / 32), blk,
-                           full, s, a);
+        launch_dec<dec_gemm1_kernel<MODE, TGM, DEPTH, true, false, 1>>(dim3(a.max_tiles, a.F / 32), full, s, a);
     } else {
-        hipLaunchKernelGGL((dec_gemm1_kernel<MODE, TGM, 2, false, false, 1>), dim3(a.max_tiles, a.F / 32), blk,
-                           dec_lds_bytes(4 * TGM, a.d, false), s, a);
+        launch_dec<dec_gemm1_kernel<MODE, TGM, 2, false, false, 1>>(dim3(a.max_tiles, a.F / 32),
+                                                                     dec_lds_bytes(4 * TGM, a.d, false), s, a);
     }
 }
 
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
-    const bool small = dec_rows(a.T, a.topk, a.E) == 4;
+    const int rows = dec_rows(a.T, a.topk, a.E);
     const bool one = g1_row_groups(a) == 1;
-    if (small) {
+    if (rows == 4) {
         if (a.mode == 0) one ? launch_g1<0, 1, kG1Depth, 1>(a, s) : launch_g1<0, 1, kG1Depth, 4>(a, s);
         else one ? launch_g1<1, 1, kG1Depth, 1>(a, s) : launch_g1<1, 1, kG1Depth, 4>(a, s);
+    } else if (rows == 8) {
+        if (a.mode == 0) one ? launch_g1<0, 2, kG1Depth, 1>(a, s) : launch_g1<0, 2, kG1Depth, 4>(a, s);
+        else one ? launch_g1<1, 2, kG1Depth, 1>(a, s) : launch_g1<1, 2, kG1Depth, 4>(a, s);
     } else {
         if (a.mode == 0) one ? launch_g1<0, 4, 2, 1>(a, s) : launch_g1<0, 4, 2, 4>(a, s);
         else one ? launch_g1<1, 4, 2, 1>(a, s) : launch_g1<1, 4, 2, 4>(a, s);
@@ -474,22 +494,21 @@ hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
 template <int TGM, int DEPTH, int RG>
 static void launch_g2(const GemmArgs& a, hipStream_t s) {
     const int full = dec_lds_bytes(4 * TGM, a.F, true);
-    const dim3 blk(64 * kDecWaves);
     constexpr bool kSeg = DEPTH % 4 == 0;
     if (full <= kFullALds) {
         const bool seg = kSeg && a.F % 1024 == 0;
         if (a.d % (16 * kDecWaves * RG) == 0) {
             const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * RG));
-            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, RG, true, kSeg>), grid, blk, full, s, a);
-            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, RG, true, false>), grid, blk, full, s, a);
+            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, kSeg>>(grid, full, s, a);
+            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, false>>(grid, full, s, a);
         } else {
             const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 2));
-            if (seg) hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg>), grid, blk, full, s, a);
-            else hipLaunchKernelGGL((dec_gemm2_kernel<TGM, DEPTH, 2, true, false>), grid, blk, full, s, a);
+            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg>>(grid, full, s, a);
+            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, false>>(grid, full, s, a);
         }
     } else {
-        hipLaunchKernelGGL((dec_gemm2_kernel<TGM, 2, 1, false, false>), dim3(a.max_tiles, a.d / (16 * kDecWaves)), blk,
-                           dec_lds_bytes(4 * TGM, a.F, false), s, a);
+        launch_dec<dec_gemm2_kernel<TGM, 2, 1, false, false>>(dim3(a.max_tiles, a.d / (16 * kDecWaves)),
+                                                               dec_lds_bytes(4 * TGM, a.F, false), s, a);
     }
 }
 
@@ -503,7 +522,9 @@ static void launch_g2_rg(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s) {
-    if (dec_rows(a.T, a.topk, a.E) == 4) launch_g2_rg<1, 4>(a, s);
+    const int rows = dec_rows(a.T, a.topk, a.E);
+    if (rows == 4) launch_g2_rg<1, 4>(a, s);
+    else if (rows == 8) launch_g2_rg<2, 4>(a, s);
     else launch_g2_rg<4, 2>(a, s);
     return hipGetLastError();
 }

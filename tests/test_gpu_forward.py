@@ -192,6 +192,44 @@ def test_full_size_sampled_rows(name):
     assert err <= tol(w.mode)
 
 
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("T", [12, 13, 36, 37])
+def test_decode_tile_heights(T, mode):
+    """Weight streaming takes 4-row tiles up to T k = 2E pairs, 8-row tiles up
+    to 6E, 16-row tiles beyond: both sides of each bound, full output."""
+    require_gpu()
+    lay = layer("mid", T=T)
+    w = lay.w
+    log(f"decode tile heights T={T} (T k / E = {T * w.k / w.E:.2f}) mode={mode}")
+    out = lay.run(w.offset, w.L, w.has_shared, mode, nv.PATH_DECODE)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, mode)
+    err = rel_err(out, ref["out"])
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(mode)
+
+
+@pytest.mark.parametrize("T", [128, 240])
+def test_full_size_decode_8_row_tiles(T):
+    """The 320-expert shard at T = 128 and 240 on weight streaming: 8-row tiles
+    whose whole-K token stage (65.7 KB) takes more than 64 KB of LDS; sampled
+    rows against the oracle."""
+    require_gpu()
+    base = workloads.WORKLOADS["decode_shard0_w4a16"]
+    lay = full_layer("decode_shard0_w4a16")
+    w = workloads.replace(base, T=T, hidden_seed=base.hidden_seed + T)
+    lay.w = w
+    lay.x = workloads.gen_hidden(w, "cuda")
+    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode)
+    assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_DECODE
+    log(f"full-size decode T={T}")
+    out = lay.run(w.offset, w.L, w.has_shared, w.mode)
+    rows = sample_rows(w.T, 3, seed=T)
+    ref, _ = lay.oracle_rows(rows, w.offset, w.L, w.has_shared, w.mode)
+    err = rel_err(out[torch.as_tensor(rows, device="cuda")], ref)
+    log(f"  sampled rows {rows.tolist()}: normwise rel err {err:.3e}")
+    assert err <= tol(w.mode)
+
+
 def test_full_size_two_shards_sum_to_unsharded_oracle():
     """Shard 0 (experts 0-159, with the shared expert) plus shard 1 (160-319) at
     the second shard's token count, W4A4, against the unsharded oracle."""
