@@ -417,12 +417,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
 }
 
 // Tile height of the decode path: 4 token rows (one group) when experts expect
-// at most ~2 tokens, 8 rows (two groups) up to ~6, else 16 rows (four groups;
+// at most ~2 tokens, 8 rows (two groups) up to ~12, else 16 rows (four groups;
 // only when the decode path is forced beyond that).  The 4- and 8-row tiles
 // stage the whole K of their token rows in LDS (up to K = 4096 for 8 rows).
+// (On the 4096 x 1024 layer, 8-row tiles take the 160-expert shard at T = 128
+// from 457 to 344 us, at T = 256 from 558 to 458 us, against 16-row tiles.)
 int dec_rows(int T, int topk, int E) {
     const long long p = (long long)T * topk;
-    return p <= 2LL * E ? 4 : (p <= 6LL * E ? 8 : 16);
+    return p <= 2LL * E ? 4 : (p <= 12LL * E ? 8 : 16);
 }
 
 // Launch of a decode kernel with `lds` bytes of dynamic LDS; above 64 KB the

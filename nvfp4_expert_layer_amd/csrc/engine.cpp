@@ -53,12 +53,13 @@ bool is_w4a4(int mode) { return mode == MOE_NVFP4_W4A4 || mode == MOE_NVFP4_W4A4
 int resolve_path(const moe_nvfp4_problem& p) {
     if (p.path == MOE_NVFP4_PATH_DECODE || p.path == MOE_NVFP4_PATH_PREFILL) return p.path;
     // expected local pairs per local expert: T * k / E (uniform routing).  The
-    // crossover was measured on the 4096 x 1024 layer: the tiled kernels stay
-    // near-flat in T while weight streaming grows with the rows per expert;
-    // packed W4A4 tiles move 3.5x fewer activation bytes and cross earlier.
+    // crossover was measured on the 4096 x 1024 layer with 160 local experts:
+    // the tiled kernels stay near-flat in T while weight streaming grows with
+    // the rows per expert; packed W4A4 tiles move 3.5x fewer activation bytes
+    // and cross earlier.
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
     const bool packed = is_w4a4(p.mode) && moe::pf_packed_ok(p.d_model, p.d_ff);
-    return per_expert <= (packed ? 2.0 : 6.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
+    return per_expert <= (packed ? 6.0 : 9.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
 }
 
 struct Plan {

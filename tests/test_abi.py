@@ -91,16 +91,16 @@ def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
 
 
 def test_resolved_path_crossover():
-    # expected local pairs per local expert T*k/E: weight streaming up to 6
-    # (W4A16, or W4A4 whose d or F is not a multiple of 256), 2 for packed W4A4
+    # expected local pairs per local expert T*k/E: weight streaming up to 9
+    # (W4A16, or W4A4 whose d or F is not a multiple of 256), 6 for packed W4A4
     def path(T, mode, d=4096, F=1024, force=nv.PATH_AUTO):
         return nv.moe_nvfp4_resolved_path(nv.make_problem(T, d, F, 320, 8, 0, 160, True, mode, force))
     assert path(64, nv.W4A16) == nv.PATH_DECODE
-    assert path(240, nv.W4A16) == nv.PATH_DECODE          # 6.0
-    assert path(241, nv.W4A16) == nv.PATH_PREFILL
-    assert path(80, nv.W4A4) == nv.PATH_DECODE            # 2.0
-    assert path(81, nv.W4A4) == nv.PATH_PREFILL
-    assert path(200, nv.W4A4, F=384) == nv.PATH_DECODE    # not packed: threshold 6
+    assert path(360, nv.W4A16) == nv.PATH_DECODE          # 9.0
+    assert path(361, nv.W4A16) == nv.PATH_PREFILL
+    assert path(240, nv.W4A4) == nv.PATH_DECODE           # 6.0
+    assert path(241, nv.W4A4) == nv.PATH_PREFILL
+    assert path(300, nv.W4A4, F=384) == nv.PATH_DECODE    # not packed: threshold 9
     assert path(8192, nv.W4A16, force=nv.PATH_DECODE) == nv.PATH_DECODE
     assert path(1, nv.W4A4, force=nv.PATH_PREFILL) == nv.PATH_PREFILL
     with pytest.raises(nv.MoeNvfp4Error):
@@ -119,7 +119,7 @@ def test_static_globals_are_validated():
     p = nv.make_problem(64, 512, 256, 24, 4, 0, 24, True, nv.W4A4, nv.PATH_AUTO, (0.0, 0.0))
     assert nv.moe_nvfp4_validate(p, 1 << 30) == nv.OK
     # the static mode resolves its path like W4A4 and needs the same workspace
-    ps = nv.make_problem(100, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4_STATIC, nv.PATH_AUTO, (0.01, 0.01))
-    pd = nv.make_problem(100, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4)
+    ps = nv.make_problem(300, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4_STATIC, nv.PATH_AUTO, (0.01, 0.01))
+    pd = nv.make_problem(300, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4)
     assert nv.moe_nvfp4_resolved_path(ps) == nv.moe_nvfp4_resolved_path(pd) == nv.PATH_PREFILL
     assert nv.moe_nvfp4_workspace_size(ps) == nv.moe_nvfp4_workspace_size(pd)
