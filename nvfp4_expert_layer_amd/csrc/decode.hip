@@ -416,15 +416,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
     dec_stream<1, TGM, DEPTH, RGS, FULLA, SEG>(s_arow, ntok, F, codes, scales, cstride, sstride, lds, epi);
 }
 
-// Tile height of the decode path: 4 token rows (one group) when experts expect
-// at most ~2 tokens, 8 rows (two groups) up to ~12, else 16 rows (four groups;
+// Tile height of the decode path: 4 token rows (one group) while experts expect
+// at most ~6 tokens, 8 rows (two groups) up to ~12, else 16 rows (four groups;
 // only when the decode path is forced beyond that).  The 4- and 8-row tiles
 // stage the whole K of their token rows in LDS (up to K = 4096 for 8 rows).
-// (On the 4096 x 1024 layer, 8-row tiles take the 160-expert shard at T = 128
-// from 457 to 344 us, at T = 256 from 558 to 458 us, against 16-row tiles.)
+// Measured on the 4096 x 1024 layer with 160 local experts: 4-row tiles beat
+// 8-row tiles up to T k / E ~ 6 (T = 128: 316 against 344 us), although an
+// expert with more than 4 pairs streams its weights once per tile; beyond,
+// 8-row tiles win (T = 288: 478 against 485 us); both beat 16-row tiles by
+// 20-30% (T = 128: 457 us).
 int dec_rows(int T, int topk, int E) {
     const long long p = (long long)T * topk;
-    return p <= 2LL * E ? 4 : (p <= 12LL * E ? 8 : 16);
+    return p <= 6LL * E ? 4 : (p <= 12LL * E ? 8 : 16);
 }
 
 // Launch of a decode kernel with `lds` bytes of dynamic LDS; above 64 KB the

@@ -193,9 +193,9 @@ def test_full_size_sampled_rows(name):
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
-@pytest.mark.parametrize("T", [12, 13, 72, 73])
+@pytest.mark.parametrize("T", [12, 36, 37, 72, 73])
 def test_decode_tile_heights(T, mode):
-    """Weight streaming takes 4-row tiles up to T k = 2E pairs, 8-row tiles up
+    """Weight streaming takes 4-row tiles up to T k = 6E pairs, 8-row tiles up
     to 12E, 16-row tiles beyond: both sides of each bound, full output."""
     require_gpu()
     lay = layer("mid", T=T)
