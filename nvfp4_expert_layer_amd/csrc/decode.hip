@@ -453,11 +453,15 @@ static double expected_tiles(const GemmArgs& a) {
 }
 
 // Row groups a wave walks back to back: long streams amortise the prefetch
-// ring's fill when many experts keep the chip busy; with few experts, one
-// row group per wave gives the grid more workgroups (measured on the
+// ring's fill when many experts keep the chip busy; with few experts, fewer
+// row groups per wave give the grid more workgroups (measured on the
 // 4096 x 1024 layer: GEMM1 at T = 1..16 -- 4..54 tiles -- runs 1.4-2.4x faster
-// with one row group, at T = 64 -- 128 tiles -- 10% slower).
-static int g1_row_groups(const GemmArgs& a) { return expected_tiles(a) <= 64.0 ? 1 : 4; }
+// with one row group than with four; at T = 24..56 -- 74..128 tiles -- two row
+// groups are up to 15% faster than four; at T = 64 -- 140 tiles -- four).
+static int g1_row_groups(const GemmArgs& a) {
+    const double t = expected_tiles(a);
+    return t <= 64.0 ? 1 : (t <= 130.0 ? 2 : 4);
+}
 static int g2_row_groups(const GemmArgs& a) {
     const double t = expected_tiles(a);
     return t <= 8.0 ? 1 : (t <= 32.0 ? 2 : 4);
@@ -480,19 +484,20 @@ static void launch_g1(const GemmArgs& a, hipStream_t s) {
     }
 }
 
+template <int MODE, int TGM, int DEPTH>
+static void launch_g1_rg(const GemmArgs& a, hipStream_t s) {
+    switch (g1_row_groups(a)) {
+        case 1: launch_g1<MODE, TGM, DEPTH, 1>(a, s); break;
+        case 2: launch_g1<MODE, TGM, DEPTH, 2>(a, s); break;
+        default: launch_g1<MODE, TGM, DEPTH, 4>(a, s); break;
+    }
+}
+
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
     const int rows = dec_rows(a.T, a.topk, a.E);
-    const bool one = g1_row_groups(a) == 1;
-    if (rows == 4) {
-        if (a.mode == 0) one ? launch_g1<0, 1, kG1Depth, 1>(a, s) : launch_g1<0, 1, kG1Depth, 4>(a, s);
-        else one ? launch_g1<1, 1, kG1Depth, 1>(a, s) : launch_g1<1, 1, kG1Depth, 4>(a, s);
-    } else if (rows == 8) {
-        if (a.mode == 0) one ? launch_g1<0, 2, kG1Depth, 1>(a, s) : launch_g1<0, 2, kG1Depth, 4>(a, s);
-        else one ? launch_g1<1, 2, kG1Depth, 1>(a, s) : launch_g1<1, 2, kG1Depth, 4>(a, s);
-    } else {
-        if (a.mode == 0) one ? launch_g1<0, 4, 2, 1>(a, s) : launch_g1<0, 4, 2, 4>(a, s);
-        else one ? launch_g1<1, 4, 2, 1>(a, s) : launch_g1<1, 4, 2, 4>(a, s);
-    }
+    if (rows == 4) a.mode == 0 ? launch_g1_rg<0, 1, kG1Depth>(a, s) : launch_g1_rg<1, 1, kG1Depth>(a, s);
+    else if (rows == 8) a.mode == 0 ? launch_g1_rg<0, 2, kG1Depth>(a, s) : launch_g1_rg<1, 2, kG1Depth>(a, s);
+    else a.mode == 0 ? launch_g1_rg<0, 4, 2>(a, s) : launch_g1_rg<1, 4, 2>(a, s);
     return hipGetLastError();
 }
 

@@ -208,11 +208,12 @@ def test_decode_tile_heights(T, mode):
     assert err <= tol(mode)
 
 
-@pytest.mark.parametrize("T", [128, 360])
-def test_full_size_decode_8_row_tiles(T):
-    """The 320-expert shard at T = 128 and 360 on weight streaming: 8-row tiles
-    whose whole-K token stage (65.7 KB) takes more than 64 KB of LDS; sampled
-    rows against the oracle."""
+@pytest.mark.parametrize("T", [32, 128, 360])
+def test_full_size_decode_other_token_counts(T):
+    """The 320-expert shard on weight streaming at T = 32 (two row groups per
+    wave in GEMM1), 128 (4-row tiles at 4 pairs per expert) and 360 (8-row
+    tiles, whose whole-K token stage of 65.7 KB takes more than 64 KB of LDS);
+    sampled rows against the oracle."""
     require_gpu()
     base = workloads.WORKLOADS["decode_shard0_w4a16"]
     lay = full_layer("decode_shard0_w4a16")
