@@ -29,7 +29,6 @@
 // Layer semantics: the page "Serving Solar Open 2 on DGX Spark", sections "수정
 // 사항 › b12x에서의 Expert Parallelism 구현 추가" and "b12x 버전이 실제 NVFP4
 // 체크포인트를 읽어들이도록 만들기".
-#include <atomic>
 #include <cmath>
 #include "device_common.h"
 #include "kernels.h"
@@ -430,16 +429,11 @@ int dec_rows(int T, int topk, int E) {
     return p <= 6LL * E ? 4 : (p <= 12LL * E ? 8 : 16);
 }
 
-// Launch of a decode kernel with `lds` bytes of dynamic LDS; above 64 KB the
-// kernel's attribute is raised first (once per kernel; a failure is left for
-// hipGetLastError, like a failed launch).
+// Launch of a decode kernel with `lds` bytes of dynamic LDS (above 64 KB the
+// kernel's limit is raised first; a failure is left for hipGetLastError).
 template <auto Kern>
 static void launch_dec(dim3 grid, int lds, hipStream_t s, const GemmArgs& a) {
-    static std::atomic<int> allowed{65536};
-    if (lds > allowed.load(std::memory_order_relaxed) &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds) ==
-            hipSuccess)
-        allowed.store(lds, std::memory_order_relaxed);
+    if (allow_dynamic_lds<Kern>(lds) != hipSuccess) return;
     hipLaunchKernelGGL(Kern, grid, dim3(64 * kDecWaves), lds, s, a);
 }
 

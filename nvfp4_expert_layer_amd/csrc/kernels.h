@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
 
 struct ExpertWeights {            // device pointers, n experts, expert-major
@@ -98,5 +100,22 @@ hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s);
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// Raise kernel Kern's dynamic-LDS limit to `bytes` on the current device when
+// that is above the 64 KB default; the attribute is per device, so the largest
+// size set so far is kept per device and each is set once.
+template <auto Kern>
+inline hipError_t allow_dynamic_lds(int bytes) {
+    static std::atomic<int> allowed[64];
+    if (bytes <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (allowed[dev].load(std::memory_order_relaxed) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) allowed[dev].store(bytes, std::memory_order_relaxed);
+    return e;
+}
 
 }  // namespace moe

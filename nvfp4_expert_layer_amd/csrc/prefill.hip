@@ -632,13 +632,8 @@ constexpr int kQWaves = 8;
 
 template <int KIND>
 static hipError_t launch_pf4(const GemmArgs& a, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pf4_gemm_kernel<KIND, kQWaves>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = allow_dynamic_lds<pf4_gemm_kernel<KIND, kQWaves>>(kQLds);
+    if (e != hipSuccess) return e;
     const int NT = KIND == 1 ? (2 * a.F) / kPN : a.d / kPN;
     const long long n = (long long)a.max_tiles * NT;
     const long long grid = (n + 7) / 8 * 8;
@@ -649,13 +644,8 @@ static hipError_t launch_pf4(const GemmArgs& a, hipStream_t s) {
 
 template <int KIND, int MODE>
 static hipError_t launch_pf(const GemmArgs& a, hipStream_t s) {
-    static bool attr_set = false;   // per process; the attribute is per function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)pf_gemm_kernel<KIND, MODE>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e = allow_dynamic_lds<pf_gemm_kernel<KIND, MODE>>(kPLds);
+    if (e != hipSuccess) return e;
     const int NT = KIND == 1 ? (2 * a.F) / kPN : (a.d + kPN - 1) / kPN;
     const long long n = (long long)a.max_tiles * NT;
     const long long grid = (n + 7) / 8 * 8;
