@@ -62,9 +62,12 @@ def test_graph_replays_match_eager_mid(mode, path):
     _graph_vs_eager(lay, 4, 16, True, mode, path)
 
 
-def test_graph_replays_match_eager_decode_shard():
+@pytest.mark.parametrize("T", [64, 256])
+def test_graph_replays_match_eager_decode_shard(T):
+    """T = 64: exact routing, 4-row weight-streaming tiles; T = 256: certified
+    routing, one-workgroup permutation, 8-row tiles with more than 64 KB of LDS."""
     require_gpu()
-    w = workloads.WORKLOADS["decode_shard0_w4a16"]
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     lay = Layer(w, experts_range=(0, w.L))
-    log("graph replay decode shard T=64")
+    log(f"graph replay decode shard T={T}")
     _graph_vs_eager(lay, w.offset, w.L, True, w.mode, nv.PATH_AUTO)
