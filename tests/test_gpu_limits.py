@@ -77,6 +77,23 @@ def test_route_1024_experts_widest_model(T):
     assert P == T * 32
 
 
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("T,d", [(10, 16384), (30, 8192), (30, 4096)], ids=["4row-chunked", "8row-chunked", "8row-whole"])
+def test_decode_token_stage_variants(T, d, mode):
+    """Weight streaming whose token stage does not fit in LDS whole: 4-row tiles
+    at K = 16384 and 8-row tiles at K = 8192 stage 512-element chunks; 8-row
+    tiles at K = 4096 stage the whole K (65.7 KB of LDS).  Full output."""
+    require_gpu()
+    lay = get(workloads.replace(WIDE_D, name=f"stage_{T}_{d}", T=T, d=d))
+    w = lay.w
+    log(f"decode token stage T={T} d={d} mode={mode}")
+    out = lay.run(w.offset, w.L, w.has_shared, mode, nv.PATH_DECODE)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, mode)["out"]
+    err = rel_err(out, ref)
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(mode)
+
+
 @pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
 def test_layer_1024_local_experts_top32(path):
     require_gpu()
