@@ -306,6 +306,26 @@ __device__ __forceinline__ DecTile dec_tile(const GemmArgs& a) {
     return t;
 }
 
+// MERGE consecutive table tiles of one group as one workgroup's rows: the tile
+// whose index within its group is a multiple of MERGE takes the rows of the
+// next MERGE - 1 tiles of the same group too; the others return (false).
+template <int MERGE>
+__device__ __forceinline__ bool dec_merge_tiles(const GemmArgs& a, DecTile& t) {
+    if (MERGE == 1) return true;
+    const int4 t0 = a.tiles[blockIdx.x];
+    if (t0.w % MERGE != 0) return false;
+    const int nt = *a.ntiles;
+#pragma unroll
+    for (int m = 1; m < MERGE; ++m) {
+        const int x = (int)blockIdx.x + m;
+        if (x >= nt) break;
+        const int4 tn = a.tiles[x];
+        if (tn.x != t0.x) break;
+        t.re = tn.z;
+    }
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // GEMM1 + SwiGLU: a workgroup = 32 RG SwiGLU columns of a tile of <= 4 TGM
 // token rows; in row group j < RG, waves 0,1 stream the gate rows of columns
@@ -380,15 +400,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // GEMM2: a wave walks RGS groups of 16 output columns (16 rows of w2 each); the
-// workgroup covers 16 * kDecWaves * RGS columns.  grid (max_tiles, d / that).
+// workgroup covers 16 * kDecWaves * RGS columns of the rows of MERGE table
+// tiles (at most 4 TGM rows).  grid (max_tiles, d / that).
 // ---------------------------------------------------------------------------
-template <int TGM, int DEPTH, int RGS, bool FULLA, bool SEG>
+template <int TGM, int DEPTH, int RGS, bool FULLA, bool SEG, int MERGE>
 __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
     constexpr int ROWS = 4 * TGM;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     __shared__ const uint16_t* s_arow[ROWS];
     if ((int)blockIdx.x >= *a.ntiles) return;
-    const DecTile tl = dec_tile(a);
+    DecTile tl = dec_tile(a);
+    if (!dec_merge_tiles<MERGE>(a, tl)) return;
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
     const int d = a.d, F = a.F;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -495,7 +517,9 @@ hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int TGM, int DEPTH, int RG>
+// TGM: token groups of the kernel (4 TGM rows); the table's tiles are 4 TGM /
+// MERGE rows high.
+template <int TGM, int DEPTH, int RG, int MERGE>
 static void launch_g2(const GemmArgs& a, hipStream_t s) {
     const int full = dec_lds_bytes(4 * TGM, a.F, true);
     constexpr bool kSeg = DEPTH % 4 == 0;
@@ -503,33 +527,45 @@ static void launch_g2(const GemmArgs& a, hipStream_t s) {
         const bool seg = kSeg && a.F % 1024 == 0;
         if (a.d % (16 * kDecWaves * RG) == 0) {
             const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * RG));
-            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, kSeg>>(grid, full, s, a);
-            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, false>>(grid, full, s, a);
+            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, kSeg, MERGE>>(grid, full, s, a);
+            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, RG, true, false, MERGE>>(grid, full, s, a);
         } else {
             const dim3 grid(a.max_tiles, a.d / (16 * kDecWaves * 2));
-            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg>>(grid, full, s, a);
-            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, false>>(grid, full, s, a);
+            if (seg) launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, kSeg, MERGE>>(grid, full, s, a);
+            else launch_dec<dec_gemm2_kernel<TGM, DEPTH, 2, true, false, MERGE>>(grid, full, s, a);
         }
     } else {
-        launch_dec<dec_gemm2_kernel<TGM, 2, 1, false, false>>(dim3(a.max_tiles, a.d / (16 * kDecWaves)),
-                                                               dec_lds_bytes(4 * TGM, a.F, false), s, a);
+        launch_dec<dec_gemm2_kernel<TGM, 2, 1, false, false, MERGE>>(dim3(a.max_tiles, a.d / (16 * kDecWaves)),
+                                                                      dec_lds_bytes(4 * TGM, a.F, false), s, a);
     }
 }
 
-template <int TGM, int DEPTH>
+template <int TGM, int DEPTH, int MERGE>
 static void launch_g2_rg(const GemmArgs& a, hipStream_t s) {
     switch (g2_row_groups(a)) {
-        case 1: launch_g2<TGM, DEPTH, 1>(a, s); break;
-        case 2: launch_g2<TGM, DEPTH, 2>(a, s); break;
-        default: launch_g2<TGM, DEPTH, 4>(a, s); break;
+        case 1: launch_g2<TGM, DEPTH, 1, MERGE>(a, s); break;
+        case 2: launch_g2<TGM, DEPTH, 2, MERGE>(a, s); break;
+        default: launch_g2<TGM, DEPTH, 4, MERGE>(a, s); break;
     }
+}
+
+// The down projection takes 8-row tiles (two 4-row table tiles of one group)
+// where the table has 4-row tiles and experts expect more than kG2MergePairs
+// pairs.  Measured on the 4096 x 1024 layer with 160 local experts: GEMM2 at
+// T = 240 (6 pairs per expert) 132 -> 115 us; at T = 192 equal; at T <= 160
+// 7-13 us slower (the second row group of an 8-row tile is mostly empty, and
+// half the workgroups only return).  Merging 8-row table tiles into 16-row
+// tiles is slower at every T tried (256-320).
+constexpr double kG2MergePairs = 5.0;
+static bool g2_merge(const GemmArgs& a) {
+    return (double)a.T * a.topk > kG2MergePairs * a.E;
 }
 
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s) {
     const int rows = dec_rows(a.T, a.topk, a.E);
-    if (rows == 4) launch_g2_rg<1, 4>(a, s);
-    else if (rows == 8) launch_g2_rg<2, 4>(a, s);
-    else launch_g2_rg<4, 2>(a, s);
+    if (rows == 4) g2_merge(a) ? launch_g2_rg<2, 4, 2>(a, s) : launch_g2_rg<1, 4, 1>(a, s);
+    else if (rows == 8) launch_g2_rg<2, 4, 1>(a, s);
+    else launch_g2_rg<4, 2, 1>(a, s);
     return hipGetLastError();
 }
 

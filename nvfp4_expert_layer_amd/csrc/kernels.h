@@ -47,7 +47,7 @@ struct GemmArgs {
     float a1g, a2g;               // activation global scales of the GEMM1 / GEMM2 inputs
                                   //   (1 unless static W4A4); GEMM inputs hold code * scale
     const int32_t* perm;          // [T*k]
-    const int4* tiles;            // (group, row_begin, row_end, -)
+    const int4* tiles;            // (group, row_begin, row_end, index within the group)
     const int32_t* ntiles;
     int max_tiles;
     const uint16_t* hidden;       // bf16 [T][d]

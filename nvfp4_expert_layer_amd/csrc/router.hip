@@ -612,8 +612,8 @@ __global__ __launch_bounds__(kPermBlock) void perm_block_kernel(
 
 // ---------------------------------------------------------------------------
 // P2: one workgroup.  block_counts -> per-block bases (in place), counts,
-// offsets, and the GEMM tile table (group, row_begin, row_end) with BM rows per
-// tile.  Groups 0..L-1 are the local experts (rows [offsets[g], offsets[g+1])
+// offsets, and the GEMM tile table (group, row_begin, row_end, index of the tile
+// within its group) with BM rows per tile.  Groups 0..L-1 are the local experts (rows [offsets[g], offsets[g+1])
 // of the permuted-pair row space), group L the shared expert (rows [Tk, Tk+T)).
 // ---------------------------------------------------------------------------
 // Block-wide exclusive scans of (count, tiles) over 1024 threads (one per expert),
@@ -643,7 +643,7 @@ __device__ void scan_and_emit_tiles(int c, int L, int T, int topk, int has_share
         if (s_off) s_off[tid] = exc;
         for (int i = 0; i < tc; ++i) {
             const int rb = exc + i * BM;
-            tiles[ext + i] = make_int4(tid, rb, min(rb + BM, exc + c), 0);
+            tiles[ext + i] = make_int4(tid, rb, min(rb + BM, exc + c), i);
         }
     }
     if (tid == L - 1) {
@@ -653,7 +653,7 @@ __device__ void scan_and_emit_tiles(int c, int L, int T, int topk, int has_share
             const int base = T * topk;
             const int st = (T + BM - 1) / BM;
             for (int i = 0; i < st; ++i)
-                tiles[n + i] = make_int4(L, base + i * BM, min(base + (i + 1) * BM, base + T), 0);
+                tiles[n + i] = make_int4(L, base + i * BM, min(base + (i + 1) * BM, base + T), i);
             n += st;
         }
         ntiles[0] = n < max_tiles ? n : max_tiles;

@@ -193,10 +193,11 @@ def test_full_size_sampled_rows(name):
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
-@pytest.mark.parametrize("T", [12, 36, 37, 72, 73])
+@pytest.mark.parametrize("T", [12, 30, 31, 36, 37, 72, 73])
 def test_decode_tile_heights(T, mode):
     """Weight streaming takes 4-row tiles up to T k = 6E pairs, 8-row tiles up
-    to 12E, 16-row tiles beyond: both sides of each bound, full output."""
+    to 12E, 16-row tiles beyond; above 5E pairs the down projection merges two
+    4-row tiles of one expert: both sides of each bound, full output."""
     require_gpu()
     lay = layer("mid", T=T)
     w = lay.w
@@ -208,12 +209,13 @@ def test_decode_tile_heights(T, mode):
     assert err <= tol(mode)
 
 
-@pytest.mark.parametrize("T", [32, 128, 360])
+@pytest.mark.parametrize("T", [32, 128, 240, 360])
 def test_full_size_decode_other_token_counts(T):
     """The 320-expert shard on weight streaming at T = 32 (two row groups per
-    wave in GEMM1), 128 (4-row tiles at 4 pairs per expert) and 360 (8-row
-    tiles, whose whole-K token stage of 65.7 KB takes more than 64 KB of LDS);
-    sampled rows against the oracle."""
+    wave in GEMM1), 128 (4-row tiles at 4 pairs per expert), 240 (6 pairs per
+    expert: the down projection merges two 4-row tiles) and 360 (8-row tiles,
+    whose whole-K token stage of 65.7 KB takes more than 64 KB of LDS); sampled
+    rows against the oracle."""
     require_gpu()
     base = workloads.WORKLOADS["decode_shard0_w4a16"]
     lay = full_layer("decode_shard0_w4a16")
