@@ -109,6 +109,27 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _ptrs(*specs):
+    """Device pointers of the tensors of specs (tensor, name, dtype, shape), after
+    checking every tensor's dtype and shape (a None entry of `shape` matches any
+    size) -- the library reads and writes exactly these extents, so a smaller
+    tensor would be accessed out of bounds.  None tensors pass as NULL."""
+    for t, name, dtype, shape in specs:
+        if t is None:
+            continue
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if t.dim() != len(shape) or any(s is not None and t.shape[i] != s for i, s in enumerate(shape)):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return [_ptr(t) for t, *_ in specs]
+
+
+def _rows(p):
+    """Row count of the token tensors of problem p: T (any, when T = 0: an empty
+    batch reads nothing, but the library still wants non-NULL pointers)."""
+    return p.num_tokens if p.num_tokens > 0 else None
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -131,9 +152,23 @@ class NVFP4Experts:
     w2_scale: torch.Tensor    # uint8 [n, d, F/16]
     w2_global: torch.Tensor   # fp32 [n]
 
-    def c_struct(self):
+    def c_struct(self, n=None, d=None, F=None, name="experts"):
+        """The C view; with n, d, F given, the tensors are first checked against
+        n experts of a d x F layer (dtype, shape, GPU, contiguity)."""
+        if n is not None:
+            _ptrs(*self.specs(n, d, F, name))
         return moe_nvfp4_weights(*(t.data_ptr() for t in (
             self.w13, self.w13_scale, self.w13_global, self.w2, self.w2_scale, self.w2_global)))
+
+    def specs(self, n, d, F, name):
+        """(tensor, name, dtype, shape) of each tensor for n experts of a d x F layer."""
+        u8, f32 = torch.uint8, torch.float32
+        return [(self.w13, f"{name}.w13", u8, (n, 2 * F, d // 2)),
+                (self.w13_scale, f"{name}.w13_scale", u8, (n, 2 * F, d // 16)),
+                (self.w13_global, f"{name}.w13_global", f32, (n,)),
+                (self.w2, f"{name}.w2", u8, (n, d, F // 2)),
+                (self.w2_scale, f"{name}.w2_scale", u8, (n, d, F // 16)),
+                (self.w2_global, f"{name}.w2_global", f32, (n,))]
 
     def slice(self, start, count):
         """Experts [start, start+count) (views; any start is accepted by the library)."""
@@ -198,14 +233,26 @@ def alloc_workspace(problem, device="cuda"):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def moe_nvfp4_forward(problem, hidden, gate_w, local, shared, workspace, out, stream=None):
-    """hidden bf16 [T, d]; gate_w bf16 [E, d]; local/shared: NVFP4Experts (shared may be
-    None); workspace uint8 device tensor; out bf16 [T, d] (overwritten)."""
+def _forward_args(p, hidden, gate_w, local, shared, workspace, out):
+    T, d, F, bf = _rows(p), p.d_model, p.d_ff, torch.bfloat16
+    specs = [(hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)),
+             (workspace, "workspace", torch.uint8, (None,)), (out, "out", bf, (T, d))]
+    specs += local.specs(p.num_local_experts, d, F, "local")
+    if shared is not None:
+        specs += shared.specs(1, d, F, "shared")
+    h, g, ws, o = _ptrs(*specs)[:4]
     lw = local.c_struct()
     sw = shared.c_struct() if shared is not None else None
-    _check(lib().moe_nvfp4_forward(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), ctypes.byref(lw),
-                                   ctypes.byref(sw) if sw is not None else None, _ptr(workspace),
-                                   workspace.numel(), _ptr(out), _stream(stream)))
+    return (ctypes.byref(p), h, g, ctypes.byref(lw), ctypes.byref(sw) if sw is not None else None,
+            ws, workspace.numel(), o)
+
+
+def moe_nvfp4_forward(problem, hidden, gate_w, local, shared, workspace, out, stream=None):
+    """hidden bf16 [T, d]; gate_w bf16 [E, d]; local/shared: NVFP4Experts of L and 1
+    experts (shared may be None); workspace uint8 [n] device tensor; out bf16 [T, d]
+    (overwritten).  Tensors of another dtype or shape raise ValueError."""
+    _check(lib().moe_nvfp4_forward(*_forward_args(problem, hidden, gate_w, local, shared, workspace, out),
+                                   _stream(stream)))
     return out
 
 
@@ -213,41 +260,56 @@ def moe_nvfp4_forward_timed(problem, hidden, gate_w, local, shared, workspace, o
                             stream=None):
     """moe_nvfp4_forward recording raw hipEvent_t handles (ints, or None) at the
     kernel boundaries; see the header for the event slots."""
-    lw = local.c_struct()
-    sw = shared.c_struct() if shared is not None else None
+    args = _forward_args(problem, hidden, gate_w, local, shared, workspace, out)
     arr = (ctypes.c_void_p * len(events))(*[e if e else None for e in events])
-    _check(lib().moe_nvfp4_forward_timed(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), ctypes.byref(lw),
-                                         ctypes.byref(sw) if sw is not None else None, _ptr(workspace),
-                                         workspace.numel(), _ptr(out), _stream(stream), arr, len(events)))
+    _check(lib().moe_nvfp4_forward_timed(*args, _stream(stream), arr, len(events)))
     return out
 
 
 def moe_nvfp4_route(problem, hidden, gate_w, workspace, topk_ids=None, topk_w=None, counts=None,
                     offsets=None, perm=None, stream=None):
-    _check(lib().moe_nvfp4_route(ctypes.byref(problem), _ptr(hidden), _ptr(gate_w), _ptr(topk_ids),
-                                 _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(workspace),
-                                 workspace.numel(), _stream(stream)))
+    """Routing and permutation only.  hidden bf16 [T, d], gate_w bf16 [E, d];
+    optional outputs topk_ids int32 [T, k], topk_w fp32 [T, k], counts int32 [L],
+    offsets int32 [L + 1], perm int32 [T k]."""
+    p, i32 = problem, torch.int32
+    T, k, L = _rows(p), p.top_k, p.num_local_experts
+    ptrs = _ptrs((hidden, "hidden", torch.bfloat16, (T, p.d_model)),
+                 (gate_w, "gate_w", torch.bfloat16, (p.num_experts, p.d_model)),
+                 (topk_ids, "topk_ids", i32, (T, k)), (topk_w, "topk_w", torch.float32, (T, k)),
+                 (counts, "counts", i32, (L,)), (offsets, "offsets", i32, (L + 1,)),
+                 (perm, "perm", i32, (p.num_tokens * k,)), (workspace, "workspace", torch.uint8, (None,)))
+    _check(lib().moe_nvfp4_route(ctypes.byref(p), *ptrs, workspace.numel(), _stream(stream)))
 
 
 def moe_nvfp4_quantize_weights(w, codes, scales, global_scale, stream=None):
     """w bf16 [n, R, C] -> codes uint8 [n, R, C/2], scales uint8 [n, R, C/16], global fp32 [n]."""
     n, R, C = w.shape
-    _check(lib().moe_nvfp4_quantize_weights(_ptr(w), n, R, C, _ptr(codes), _ptr(scales),
-                                            _ptr(global_scale), _stream(stream)))
+    u8 = torch.uint8
+    pw, pc, ps, pg = _ptrs((w, "w", torch.bfloat16, (n, R, C)), (codes, "codes", u8, (n, R, C // 2)),
+                           (scales, "scales", u8, (n, R, C // 16)),
+                           (global_scale, "global_scale", torch.float32, (n,)))
+    _check(lib().moe_nvfp4_quantize_weights(pw, n, R, C, pc, ps, pg, _stream(stream)))
+
+
+def _act_ptrs(x, codes, scales):
+    R, C = x.shape
+    return _ptrs((x, "x", torch.bfloat16, (R, C)), (codes, "codes", torch.uint8, (R, C // 2)),
+                 (scales, "scales", torch.uint8, (R, C // 16)))
 
 
 def moe_nvfp4_quantize_activations(x, codes, scales, stream=None):
     """x bf16 [R, C] -> codes uint8 [R, C/2], scales uint8 [R, C/16]."""
     R, C = x.shape
-    _check(lib().moe_nvfp4_quantize_activations(_ptr(x), R, C, _ptr(codes), _ptr(scales), _stream(stream)))
+    px, pc, ps = _act_ptrs(x, codes, scales)
+    _check(lib().moe_nvfp4_quantize_activations(px, R, C, pc, ps, _stream(stream)))
 
 
 def moe_nvfp4_quantize_activations_static(x, g, codes, scales, stream=None):
     """Static W4A4 rule with activation global g: x bf16 [R, C] -> codes uint8
     [R, C/2], scales uint8 [R, C/16]."""
     R, C = x.shape
-    _check(lib().moe_nvfp4_quantize_activations_static(_ptr(x), R, C, float(g), _ptr(codes), _ptr(scales),
-                                                       _stream(stream)))
+    px, pc, ps = _act_ptrs(x, codes, scales)
+    _check(lib().moe_nvfp4_quantize_activations_static(px, R, C, float(g), pc, ps, _stream(stream)))
 
 
 def quantize_experts(w13, w2, out=None, start=0):
