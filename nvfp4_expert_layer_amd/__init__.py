@@ -161,7 +161,8 @@ class NVFP4Experts:
             self.w13, self.w13_scale, self.w13_global, self.w2, self.w2_scale, self.w2_global)))
 
     def specs(self, n, d, F, name):
-        """(tensor, name, dtype, shape) of each tensor for n experts of a d x F layer."""
+        """(tensor, name, dtype, shape) of each tensor for n experts (None: any
+        number) of a d x F layer."""
         u8, f32 = torch.uint8, torch.float32
         return [(self.w13, f"{name}.w13", u8, (n, 2 * F, d // 2)),
                 (self.w13_scale, f"{name}.w13_scale", u8, (n, 2 * F, d // 16)),
@@ -189,10 +190,16 @@ def moe_nvfp4_prepare(ck, global_convention, w13_order, first_expert, count, dst
     w13 in `w13_order`, global scales in `global_convention`) -> experts
     [first_expert, first_expert + count) written into `dst` (an NVFP4Experts of
     count experts, the kernel layout)."""
-    for part in (ck, dst):
-        for t in (part.w13, part.w13_scale, part.w13_global, part.w2, part.w2_scale, part.w2_global):
-            _ptr(t)   # on the GPU and contiguous
+    if ck.w13.dim() != 3:
+        raise ValueError(f"ck.w13: shape {tuple(ck.w13.shape)}, expected (E, 2F, d/2)")
     E, twoF, dh = ck.w13.shape
+    d, F = dh * 2, twoF // 2
+    # dtypes, shapes (dst holds at least `count` experts), GPU, contiguity
+    dspecs = dst.specs(None, d, F, "dst")
+    for tt, name, _, _ in dspecs:
+        if tt.dim() >= 1 and tt.shape[0] < count:
+            raise ValueError(f"{name}: {tt.shape[0]} experts, expected at least {count}")
+    _ptrs(*ck.specs(E, d, F, "ck"), *dspecs)
     c = moe_nvfp4_checkpoint(*(t.data_ptr() for t in (ck.w13, ck.w13_scale, ck.w13_global, ck.w2, ck.w2_scale,
                                                       ck.w2_global)),
                              E, dh * 2, twoF // 2, global_convention, w13_order)

@@ -470,13 +470,15 @@ static double expected_tiles(const GemmArgs& a) {
 
 // Row groups a wave walks back to back: long streams amortise the prefetch
 // ring's fill when many experts keep the chip busy; with few experts, fewer
-// row groups per wave give the grid more workgroups (measured on the
-// 4096 x 1024 layer: GEMM1 at T = 1..16 -- 4..54 tiles -- runs 1.4-2.4x faster
-// with one row group than with four; at T = 24..56 -- 74..128 tiles -- two row
-// groups are up to 15% faster than four; at T = 64 -- 140 tiles -- four).
+// row groups per wave give the grid more workgroups.  Measured on the
+// 4096 x 1024 layer with 160 local experts (expected tiles in brackets): GEMM1
+// at T = 1..16 (5..55) runs 1.4-2.4x faster with one row group than with four;
+// at T = 24..80 (75..140) two row groups are up to 15% faster than four
+// (T = 72, 80: 137, 139 against 142 us; T = 64 within 1.5%); from T = 96 (147)
+// on four are faster (T = 96: 144 against 150 us; T = 128: 175 against 182).
 static int g1_row_groups(const GemmArgs& a) {
     const double t = expected_tiles(a);
-    return t <= 64.0 ? 1 : (t <= 130.0 ? 2 : 4);
+    return t <= 64.0 ? 1 : (t <= 141.0 ? 2 : 4);
 }
 static int g2_row_groups(const GemmArgs& a) {
     const double t = expected_tiles(a);

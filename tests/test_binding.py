@@ -89,3 +89,19 @@ def test_quantizers_reject_mismatched_outputs():
     with pytest.raises(ValueError, match="must be on the GPU"):
         nv.moe_nvfp4_quantize_weights(w, torch.zeros(2, 8, 32, dtype=u8), torch.zeros(2, 8, 4, dtype=u8),
                                       torch.zeros(2, dtype=torch.float32))
+
+
+def test_prepare_checks_checkpoint_and_destination():
+    ck = nv.NVFP4Experts.empty(6, D, F, device="cpu")
+    dst = nv.NVFP4Experts.empty(2, D, F, device="cpu")
+    with pytest.raises(ValueError, match="dst.w13: 2 experts, expected at least 3"):
+        nv.moe_nvfp4_prepare(ck, 0, 0, 1, 3, dst)
+    bad = nv.NVFP4Experts.empty(2, D, F // 2, device="cpu")
+    with pytest.raises(ValueError, match="dst.w13: shape"):
+        nv.moe_nvfp4_prepare(ck, 0, 0, 1, 2, bad)
+    ck.w2_scale = ck.w2_scale[:5]
+    with pytest.raises(ValueError, match="ck.w2_scale: shape"):
+        nv.moe_nvfp4_prepare(ck, 0, 0, 1, 2, dst)
+    ck = nv.NVFP4Experts.empty(6, D, F, device="cpu")
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        nv.moe_nvfp4_prepare(ck, 0, 0, 1, 2, dst)
