@@ -17,15 +17,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (idx >= (long long)a.T * per_row) return;
     const int t = (int)(idx / per_row), c0 = (int)(idx % per_row) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto add_row = [&](size_t row, float w) {
-        const u32x4_t y = *reinterpret_cast<const u32x4_t*>(a.Y + row * a.d + c0);
-        const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s[2 * q] = fmaf(w, bf16_bits_to_f32(yw[q] & 0xFFFFu), s[2 * q]);
-            s[2 * q + 1] = fmaf(w, bf16_bits_to_f32(yw[q] >> 16), s[2 * q + 1]);
-        }
-    };
+    // the shared expert's row needs no slot lookup: its load is issued first and
+    // overlaps the slots' round trips (it is still added last)
+    u32x4_t ysh = {0u, 0u, 0u, 0u};
+    if (a.has_shared)
+        ysh = *reinterpret_cast<const u32x4_t*>(a.Y + ((size_t)a.T * a.topk + t) * a.d + c0);
     // slots in groups of 8: the group's row indices and weights first, then its
     // expert rows, so each group costs two memory round trips, not 2 per slot;
     // the sum still runs in slot order
@@ -53,7 +49,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
             }
         }
     }
-    if (a.has_shared) add_row((size_t)a.T * a.topk + t, 1.0f);
+    if (a.has_shared) {
+        const uint32_t yw[4] = {ysh.x, ysh.y, ysh.z, ysh.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s[2 * e] = fmaf(1.0f, bf16_bits_to_f32(yw[e] & 0xFFFFu), s[2 * e]);
+            s[2 * e + 1] = fmaf(1.0f, bf16_bits_to_f32(yw[e] >> 16), s[2 * e + 1]);
+        }
+    }
     u32x4_t o;
     o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
     o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
