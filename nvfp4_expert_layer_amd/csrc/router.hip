@@ -976,9 +976,12 @@ bool router_exact(int T, int E, int d) {
 
 // K slices of the exact logits: enough workgroups for the chip (about 320),
 // at most kMaxKS, each slice at least 32 elements per wave.
+// K slices of the exact logits: enough for ~640 workgroups, at most 16 (on the
+// 320-expert layer: 16 slices for every T <= 128; against a 320-workgroup
+// target, T = 65..128 took 8 and routed 2 us slower at T = 128).
 int router_exact_ksplit(int T, int E, int d) {
     const int base = ((E + 15) / 16) * ((T + 16 * kXMaxTG - 1) / (16 * kXMaxTG));
-    int ks = (320 + base - 1) / base;
+    int ks = (640 + base - 1) / base;
     if (ks > kMaxKS) ks = kMaxKS;
     if (ks > d / (32 * kXWaves)) ks = d / (32 * kXWaves);
     return ks < 1 ? 1 : ks;
