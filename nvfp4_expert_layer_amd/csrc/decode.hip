@@ -39,6 +39,7 @@ constexpr int kDecWaves = 4;        // waves per workgroup, 16 weight rows each 
 constexpr int kChunk = 512;         // K elements per LDS chunk when A is staged in chunks
 constexpr int kAPad = 8;            // bf16 padding per LDS row
 constexpr int kFullALds = 67584;    // largest whole-K A stage (bytes): 8 rows of K = 4096 fit
+constexpr int kABatch = 4;          // whole-K A stage: chunks whose loads go out together
 
 // LDS bytes of the A stage: whole K, or two chunks.
 __host__ __device__ constexpr int dec_lds_bytes(int rows, int K, bool full) {
@@ -74,23 +75,25 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     // ---- A stage: whole K once, or chunk 0 (the rest double-buffered below)
     constexpr int APT = ROWS * (kChunk / 8) / (64 * kDecWaves);   // 16-byte pieces per thread per chunk
     static_assert(APT * 64 * kDecWaves == ROWS * kChunk / 8, "A staging covers the chunk");
-    u32x4_t va[APT];
-    auto a_load = [&](int ch) {
+    auto a_load_to = [&](int ch, u32x4_t (&v)[APT]) {
 #pragma unroll
         for (int j = 0; j < APT; ++j) {
             const int piece = tid + j * (64 * kDecWaves);
             const int row = piece >> 6, col = ch * kChunk + (piece & 63) * 8;
-            if (row < ntok && col < K) va[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + col);
+            if (row < ntok && col < K) v[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + col);
         }
     };
-    auto a_store = [&](int ch, uint16_t* b) {
+    auto a_store_from = [&](int ch, const u32x4_t (&v)[APT], uint16_t* b) {
 #pragma unroll
         for (int j = 0; j < APT; ++j) {
             const int piece = tid + j * (64 * kDecWaves);
             const int row = piece >> 6, colc = (piece & 63) * 8, col = ch * kChunk + colc;
-            if (row < ntok && col < K) *reinterpret_cast<u32x4_t*>(b + row * LDW + (FULLA ? col : colc)) = va[j];
+            if (row < ntok && col < K) *reinterpret_cast<u32x4_t*>(b + row * LDW + (FULLA ? col : colc)) = v[j];
         }
     };
+    u32x4_t va[APT];
+    auto a_load = [&](int ch) { a_load_to(ch, va); };
+    auto a_store = [&](int ch, uint16_t* b) { a_store_from(ch, va, b); };
 
     // ---- weight prefetch ring.  Loads are unconditional and never selected on:
     // a prefetch past the last step re-reads the last step, and a chunk past K
@@ -151,10 +154,18 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
         for (int r = 0; r < NR; ++r) load_codes(r, u, wl[u][r], wh[u][r], ws[u][r]);
 
     if (FULLA) {
+        // the whole K in batches of kABatch chunks: a batch's loads go out
+        // together, so a workgroup waits ceil(chunks / kABatch) L2 round trips
+        // for its token rows instead of one per chunk
         const int nch = (K + kChunk - 1) / kChunk;
-        for (int ch = 0; ch < nch; ++ch) {
-            a_load(ch);
-            a_store(ch, buf0);
+        for (int ch0 = 0; ch0 < nch; ch0 += kABatch) {
+            u32x4_t vb[kABatch][APT];
+#pragma unroll
+            for (int c = 0; c < kABatch; ++c)
+                if (ch0 + c < nch) a_load_to(ch0 + c, vb[c]);
+#pragma unroll
+            for (int c = 0; c < kABatch; ++c)
+                if (ch0 + c < nch) a_store_from(ch0 + c, vb[c], buf0);
         }
         __syncthreads();
     } else {
