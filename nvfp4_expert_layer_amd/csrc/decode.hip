@@ -183,6 +183,9 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     const bool aown = (n >> 2) == g;
     const int tsub = n & 3;
     constexpr int SPC = kChunk / 256;                        // steps per LDS chunk
+    // with scale segments (K % 1024 == 0) and a 4-step ring, every row group ends
+    // on the last step of a ring round: one epilogue after the round
+    constexpr bool kEpiAfter = SEG && FULLA && DEPTH == 4;
     static_assert(FULLA || DEPTH % SPC == 0, "ring aligned with LDS chunks");
 
     auto do_step = [&](const int u, const int v) {
@@ -262,7 +265,7 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
 #pragma unroll
         for (int r = 0; r < NR; ++r) load_codes(r, v + DEPTH, wl[u][r], wh[u][r], ws[u][r]);
         if (!FULLA && si == SPC - 1 && (ch + 1) * kChunk < K) a_store(ch + 1, (ch & 1) ? buf0 : buf1);
-        if (step == nsteps - 1) {
+        if (!kEpiAfter && step == nsteps - 1) {
             epi(j, acc);
 #pragma unroll
             for (int tg = 0; tg < TGM; ++tg)
@@ -275,6 +278,16 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     for (; v0 + DEPTH <= nvirt; v0 += DEPTH) {
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) do_step(u, v0 + u);
+        if (kEpiAfter) {
+            const int v = v0 + DEPTH - 1, j = v / nsteps;
+            if (v - j * nsteps == nsteps - 1) {
+                epi(j, acc);
+#pragma unroll
+                for (int tg = 0; tg < TGM; ++tg)
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) acc[tg][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
     }
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u)
