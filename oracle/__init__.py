@@ -22,9 +22,16 @@ The NVFP4 element/scale formats themselves (E2M1 codes, one E4M3 scale per 16
 contiguous elements, fp32 per-tensor scale) are NVIDIA's published NVFP4
 definition; the pages name the format but do not define it.
 
-Arithmetic is fp64 throughout, except where a floating-point value decides an
-integer code (the quantizers): those decisions are taken in fp32, the precision
-the GPU kernels take them in, so both sides can agree bit for bit.
+Arithmetic is fp64 throughout, except inside the NVFP4 quantizers, whose scale
+arithmetic is fp32 by the format: the per-tensor global scale is an fp32 number
+(amax / (6 * 448) rounded to fp32), and the recipe derives the block scale and
+the effective decode multiplier (block scale * global) from it in that same fp32
+arithmetic, so the division that picks each E2M1 code is by that fp32 multiplier
+and is itself an fp32 operation.  For the dynamic activation scale the choice is
+immaterial: fp32(amax / 6) never lands on the other side of an E4M3 rounding
+midpoint than the exact quotient (the midpoints have at most 5 significant
+bits).  For weights, fp32(s * g) is a real choice, taken from the format's fp32
+global scale.
 
 Modules:
   nvfp4   - E2M1 / E4M3 codecs, NVFP4 weight and activation quantizers.
@@ -36,7 +43,9 @@ Modules:
             실제 NVFP4 체크포인트를 읽어들이도록 만들기".
 
 Parity status: every function here is pinned by a CPU test against the format
-definitions, closed forms, invariants or brute force (tests/test_oracle_*.py).
+definitions, closed forms, invariants or brute force (tests/test_oracle_*.py);
+`moe.forward` is pinned by `brute` (explicit loops), by the dense-FFN special
+case and by the half-shard sum, with the builtin map and with a process pool.
 End-to-end values at the workload sizes have no printed worked example on the
 pages; they are pinned only through those invariants.
 """

@@ -143,7 +143,18 @@ def dequant_expert(q):
     return w13, w2
 
 
-def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=None, act_global=(1.0, 1.0)):
+def expert_term(job):
+    """One expert's MLP over its token rows.  job = (quantized expert dict, the
+    rows of h it sees (fp64 [n, d]), mode, act_global); returns fp64 [n, d].
+    A top-level function of plain values, so that `forward` can hand the
+    independent expert terms to a process pool's map."""
+    q, h_rows, mode, act_global = job
+    w13, w2 = dequant_expert(q)
+    return expert_mlp(h_rows, w13, w2, mode, act_global)
+
+
+def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=None, act_global=(1.0, 1.0),
+            map_fn=map):
     """The fused MoE layer for one shard.
 
     x       fp64 [T, d]   (bf16 hidden, exactly widened)
@@ -152,6 +163,9 @@ def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=No
             (l in [0, num_local), i.e. global id offset + l)
     shared  quantized dict of the shared expert, or None (has_shared = 0)
     act_global  static W4A4 only: (g_a of h, g_a of the SwiGLU output)
+    map_fn  evaluates `expert_term` over the touched experts' jobs, in order
+            (the builtin map, or a process pool's); the terms are summed here in
+            local-expert order and then the shared term, whatever evaluated them
     Returns dict(out fp64 [T, d], routing..., perm...).
     """
     x = np.asarray(x, np.float64)
@@ -161,41 +175,25 @@ def forward(x, gate, experts, shared, top_k, offset, num_local, mode, routing=No
     pm = permutation(lam, num_local)
     h = quantize_input(x, mode, act_global)
     get = experts if callable(experts) else (lambda l: experts[l])
-    out = np.zeros((T, d), dtype=np.float64)
     flatw = r["weights"].reshape(-1)
-    for l in range(num_local):
-        lo, hi = pm["offsets"][l], pm["offsets"][l + 1]
-        if hi == lo:
-            continue
-        pairs = pm["perm"][lo:hi].astype(np.int64)
-        tok = pairs // top_k
-        w13, w2 = dequant_expert(get(l))
-        y = expert_mlp(h[tok], w13, w2, mode, act_global)
-        out[tok] += flatw[pairs][:, None] * y       # at most one pair per (token, expert)
+    touched = [l for l in range(num_local) if pm["offsets"][l + 1] > pm["offsets"][l]]
+    pairs_of = {l: pm["perm"][pm["offsets"][l]:pm["offsets"][l + 1]].astype(np.int64) for l in touched}
+
+    def jobs():
+        for l in touched:
+            yield (get(l), h[pairs_of[l] // top_k], mode, act_global)
+        if shared is not None:
+            yield (shared, h, mode, act_global)
+
+    out = np.zeros((T, d), dtype=np.float64)
+    terms = iter(map_fn(expert_term, jobs()))
+    for l, y in zip(touched, terms):                        # zip stops at `touched` first
+        pairs = pairs_of[l]
+        out[pairs // top_k] += flatw[pairs][:, None] * y     # at most one pair per (token, expert)
     if shared is not None:
-        w13, w2 = dequant_expert(shared)
-        out += expert_mlp(h, w13, w2, mode, act_global)
+        out += next(terms)
     return {"out": out, "ids": r["ids"], "weights": r["weights"], "logits": r["logits"],
             "ambiguous": r["ambiguous"], "local_ids": lam, **pm}
-
-
-def forward_rows(x_rows, routing_rows, experts, shared, top_k, offset, num_local, mode, act_global=(1.0, 1.0)):
-    """Output rows for a subset of tokens, given their routing (ids/weights rows).
-    Used to check sampled outputs of large problems one token at a time."""
-    x_rows = np.asarray(x_rows, np.float64)
-    h = quantize_input(x_rows, mode, act_global)
-    get = experts if callable(experts) else (lambda l: experts[l])
-    out = np.zeros_like(h)
-    for i in range(h.shape[0]):
-        for j in range(top_k):
-            lam = int(routing_rows["ids"][i, j]) - offset
-            if 0 <= lam < num_local:
-                w13, w2 = dequant_expert(get(lam))
-                out[i] += routing_rows["weights"][i, j] * expert_mlp(h[i:i + 1], w13, w2, mode, act_global)[0]
-    if shared is not None:
-        w13, w2 = dequant_expert(shared)
-        out += expert_mlp(h, w13, w2, mode, act_global)
-    return out
 
 
 def normwise_rel_err(y, y_ref):

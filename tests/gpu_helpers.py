@@ -10,7 +10,8 @@ import torch
 import nvfp4_expert_layer_amd as nv
 import workloads
 from oracle import moe
-from tests.oracle_helpers import quantize_expert_oracle, to_f64
+from tests import oracle_pool
+from tests.oracle_helpers import to_f64
 
 
 def require_gpu():
@@ -59,9 +60,23 @@ class Layer:
     def oracle_expert(self, e):
         """Oracle-quantized expert with global id e (E = the shared expert)."""
         if e not in self._oracle_cache:
-            w13, w2 = workloads.gen_expert(self.w, e, "cuda")
-            self._oracle_cache[e] = quantize_expert_oracle(w13, w2)
+            self.prefetch_oracle([e])
         return self._oracle_cache[e]
+
+    def prefetch_oracle(self, ids, batch=16):
+        """Quantize experts `ids` with the oracle on the CPU process pool: each
+        expert's bf16 draw is made on the GPU (the library's own copy comes
+        from the same draw) and its bit patterns are copied to the host."""
+        todo = sorted({int(e) for e in ids} - set(self._oracle_cache))
+        for i in range(0, len(todo), batch):
+            part = todo[i:i + batch]
+            jobs = []
+            for e in part:
+                w13, w2 = workloads.gen_expert(self.w, e, "cuda")
+                jobs.append((w13.view(torch.int16).cpu().numpy().view(np.uint16),
+                             w2.view(torch.int16).cpu().numpy().view(np.uint16)))
+            for e, q in zip(part, oracle_pool.pool_map(oracle_pool.quantize_expert_bits, jobs)):
+                self._oracle_cache[e] = q
 
     def local_weights(self, offset, L):
         assert self.lo <= offset and offset + L <= self.lo + self.n
@@ -86,18 +101,16 @@ class Layer:
         return out
 
     def oracle_full(self, offset, L, has_shared, mode, act_global=None):
+        """The oracle's whole [T, d] output for this layer's tokens (expert
+        terms on the CPU process pool, summed in the oracle's fixed order)."""
         act_global = self.w.act_global if act_global is None else act_global
-        return moe.forward(self.x64, self.G64, lambda l: self.oracle_expert(offset + l),
-                           self.oracle_expert(self.w.E) if has_shared else None,
-                           self.w.k, offset, L, mode, act_global=act_global)
-
-    def oracle_rows(self, rows, offset, L, has_shared, mode, act_global=None):
-        act_global = self.w.act_global if act_global is None else act_global
-        xr = self.x64[rows]
-        r = moe.route(xr, self.G64, self.w.k)
-        return moe.forward_rows(xr, r, lambda l: self.oracle_expert(offset + l),
-                                self.oracle_expert(self.w.E) if has_shared else None,
-                                self.w.k, offset, L, mode, act_global=act_global), r
+        r = moe.route(self.x64, self.G64, self.w.k)
+        ids = r["ids"].reshape(-1)
+        need = [int(e) for e in np.unique(ids[(ids >= offset) & (ids < offset + L)])]
+        self.prefetch_oracle(need + ([self.w.E] if has_shared else []))
+        return oracle_pool.forward(self.x64, self.G64, lambda l: self.oracle_expert(offset + l),
+                                   self.oracle_expert(self.w.E) if has_shared else None,
+                                   self.w.k, offset, L, mode, routing=r, act_global=act_global)
 
 
 def rel_err(gpu_bf16, ref64):
@@ -108,6 +121,3 @@ def tol(mode):
     return 1e-2 if mode == workloads.W4A16 else 3e-2
 
 
-def sample_rows(T, n, seed):
-    rng = np.random.default_rng(seed)
-    return np.sort(rng.choice(T, size=min(n, T), replace=False))

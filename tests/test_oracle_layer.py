@@ -173,3 +173,43 @@ def test_ambiguity_flag():
     assert r["ambiguous"][0]
     G = np.array([[2.0, 1.0, 0.5, 0.0]])
     assert not moe.route(x, G, 2)["ambiguous"][0]
+
+
+@pytest.mark.parametrize("mode", [moe.W4A16, moe.W4A4, moe.W4A4_STATIC])
+@pytest.mark.parametrize("offset,L,with_shared", [(0, 8, True), (3, 4, False), (6, 2, True)])
+def test_forward_on_a_process_pool_is_bit_identical(mode, offset, L, with_shared):
+    """The expert terms evaluated by a process pool (as the full-size parity
+    tests do) sum to exactly the serial result, and both equal the brute-force
+    loops (W4A16 / dynamic W4A4)."""
+    from tests import oracle_pool
+    w, x, G, experts, shared = tiny_problem(T=12, d=64, F=32, E=8, k=3, seed=23)
+    sh = shared if with_shared else None
+    ag = (0.0021, 0.0043) if mode == moe.W4A4_STATIC else (1.0, 1.0)
+    serial = moe.forward(x, G, experts[offset:offset + L], sh, w.k, offset, L, mode, act_global=ag)["out"]
+    pooled = oracle_pool.forward(x, G, experts[offset:offset + L], sh, w.k, offset, L, mode,
+                                 act_global=ag)["out"]
+    listed = moe.forward(x, G, experts[offset:offset + L], sh, w.k, offset, L, mode, act_global=ag,
+                         map_fn=lambda f, it: list(map(f, it)))["out"]
+    assert np.array_equal(serial, pooled)
+    assert np.array_equal(serial, listed)
+    if mode != moe.W4A4_STATIC:
+        ref = np.array(brute.layer(x.tolist(), G.tolist(), experts[offset:offset + L], sh, w.k,
+                                   offset, L, w4a4=mode == moe.W4A4))
+        assert np.max(np.abs(pooled - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_pool_quantizer_matches_the_oracle_helper():
+    """The pool's quantizer of bf16 bit patterns equals the oracle's quantizer of
+    the same values (the tests' host-side path)."""
+    import torch
+    from tests import oracle_pool
+    from tests.oracle_helpers import quantize_expert_oracle
+    g = torch.Generator().manual_seed(5)
+    w13 = (torch.randn(64, 96, generator=g) / 10).to(torch.bfloat16)
+    w2 = (torch.randn(96, 32, generator=g) / 6).to(torch.bfloat16)
+    a = quantize_expert_oracle(w13, w2)
+    b = list(oracle_pool.pool_map(oracle_pool.quantize_expert_bits,
+                                  [(w13.view(torch.int16).numpy().view(np.uint16),
+                                    w2.view(torch.int16).numpy().view(np.uint16))]))[0]
+    for key in a:
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
