@@ -69,6 +69,19 @@
  *   - Argument errors are reported before anything is enqueued.  A HIP launch
  *     failure returns MOE_NVFP4_ERR_HIP.  No exception crosses the ABI.
  *     moe_nvfp4_last_error() gives a message for the calling thread.
+ *
+ * Three layout choices differ from the most literal form of the operation
+ * (logits = hidden x gate_w with gate_w as a [d_model][E] matrix; one array of
+ * (w13, w2) global-scale pairs; any d_ff that is a multiple of the 16-element
+ * block):
+ *   - gate_w is [E][d_model], one contiguous row per routed expert, so that the
+ *     router streams each expert's row along K like the token rows (the [d][E]
+ *     matrix is its transpose; the logits are the same);
+ *   - the global scales are two fp32 arrays, w13_global[n] and w2_global[n],
+ *     one per GEMM, instead of one interleaved [n][2] array: each GEMM reads
+ *     one contiguous array, and a shard's slice is a pointer offset in each;
+ *   - d_model and d_ff must be multiples of 128 (not only of 16): both kernel
+ *     paths cover 128 SwiGLU columns (and 128 K elements) per unit of work.
  */
 #ifndef MOE_NVFP4_H
 #define MOE_NVFP4_H
@@ -97,10 +110,11 @@ typedef enum {
 
 /* Kernel path.  AUTO picks from the expected number of local pairs per local
  * expert, T * top_k / num_experts (the shard's expected load, not the global
- * one): weight-streaming kernels up to 6 (W4A16) or 2 (W4A4 with d and F
- * multiples of 256, whose tiled kernels move the activations as NVFP4), tiled
- * kernels above.  Both paths give results within the stated tolerances; they
- * are not bit-identical to each other. */
+ * one): weight-streaming kernels up to 9 (W4A16, and W4A4 when d or F is not a
+ * multiple of 256) or up to 6 (W4A4 with d and F multiples of 256, whose tiled
+ * kernels move the activations as NVFP4), tiled kernels above.  Both paths give
+ * results within the stated tolerances; they are not bit-identical to each
+ * other. */
 typedef enum {
     MOE_NVFP4_PATH_AUTO = 0,
     MOE_NVFP4_PATH_DECODE = 1,
