@@ -187,6 +187,26 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem *p, const void *hidden, cons
                             void *workspace, size_t workspace_bytes, void *out, void *stream,
                             void *const *events, int num_events);
 
+/* moe_nvfp4_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the scratch is a library-owned device array of
+ * MOE_NVFP4_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held from the first call
+ * on a device until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); the caller passes inputs and outputs
+ * as for moe_nvfp4_forward, and the result is the same.
+ *   - A problem whose workspace (moe_nvfp4_workspace_size) exceeds the scratch
+ *     returns MOE_NVFP4_ERR_WORKSPACE_TOO_SMALL before anything is enqueued
+ *     (e.g. the 4096 x 1024, 320-expert layer fits up to a few hundred tokens).
+ *   - Every call on one device shares that device's scratch: calls that overlap
+ *     on one device (other streams, other host threads) race and must be
+ *     serialized by the caller.  Nothing is assumed of the scratch's previous
+ *     contents: each call clears what it needs with kernels.
+ * Other statuses as for moe_nvfp4_forward. */
+#define MOE_NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_nvfp4_forward_noalloc(const moe_nvfp4_problem *p, const void *hidden, const void *gate_w,
+                              const moe_nvfp4_weights *local, const moe_nvfp4_weights *shared,
+                              void *out, void *stream);
+
 /* Routing and permutation only (the first steps of the forward), for checking:
  *   topk_ids  int32 [T][k]   global expert ids, slot 0 = largest logit
  *   topk_w    fp32  [T][k]   routing weights (sum to 1 per token)

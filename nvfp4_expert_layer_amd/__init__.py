@@ -77,6 +77,8 @@ def lib():
         L.moe_nvfp4_forward_timed.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
                                               P(moe_nvfp4_weights), vp, sz, vp, vp,
                                               P(ctypes.c_void_p), ctypes.c_int]
+        L.moe_nvfp4_forward_noalloc.argtypes = [P(moe_nvfp4_problem), vp, vp, P(moe_nvfp4_weights),
+                                                P(moe_nvfp4_weights), vp, vp]
         L.moe_nvfp4_route.argtypes = [P(moe_nvfp4_problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_nvfp4_quantize_weights.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.moe_nvfp4_quantize_activations.argtypes = [vp, i32, i32, vp, vp, vp]
@@ -86,7 +88,7 @@ def lib():
         L.moe_nvfp4_strerror.restype = ctypes.c_char_p
         L.moe_nvfp4_last_error.argtypes = []
         L.moe_nvfp4_last_error.restype = ctypes.c_char_p
-        for f in ("workspace_size", "validate", "forward", "forward_timed", "route", "quantize_weights",
+        for f in ("workspace_size", "validate", "forward", "forward_timed", "forward_noalloc", "route", "quantize_weights",
                   "quantize_activations", "quantize_activations_static", "prepare", "resolved_path"):
             getattr(L, "moe_nvfp4_" + f).restype = ctypes.c_int
         _lib = L
@@ -270,6 +272,26 @@ def moe_nvfp4_forward_timed(problem, hidden, gate_w, local, shared, workspace, o
     args = _forward_args(problem, hidden, gate_w, local, shared, workspace, out)
     arr = (ctypes.c_void_p * len(events))(*[e if e else None for e in events])
     _check(lib().moe_nvfp4_forward_timed(*args, _stream(stream), arr, len(events)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # MOE_NVFP4_NOALLOC_SCRATCH_BYTES
+
+
+def moe_nvfp4_forward_noalloc(problem, hidden, gate_w, local, shared, out, stream=None):
+    """moe_nvfp4_forward without a workspace: the library's own per-device
+    scratch (NOALLOC_SCRATCH_BYTES) serves; problems needing more raise.  Calls
+    that overlap on one device race (they share the scratch)."""
+    p, T, d, F, bf = problem, _rows(problem), problem.d_model, problem.d_ff, torch.bfloat16
+    specs = [(hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)), (out, "out", bf, (T, d))]
+    specs += local.specs(p.num_local_experts, d, F, "local")
+    if shared is not None:
+        specs += shared.specs(1, d, F, "shared")
+    h, g, o = _ptrs(*specs)[:3]
+    lw = local.c_struct()
+    sw = shared.c_struct() if shared is not None else None
+    _check(lib().moe_nvfp4_forward_noalloc(ctypes.byref(p), h, g, ctypes.byref(lw),
+                                           ctypes.byref(sw) if sw is not None else None, o, _stream(stream)))
     return out
 
 

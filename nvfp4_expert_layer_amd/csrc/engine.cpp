@@ -211,6 +211,32 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     return hip_status(moe::launch_permute(q, s), "permutation launch");
 }
 
+// Scratch of the no-allocation forward: one array per device (each GPU the
+// library runs on holds its own copy until the process ends).  Host code never
+// uses the array's name as an address: it is a host-side stand-in; the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = MOE_NVFP4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device `dev` (looked up on the
+// first call on that device, with that device current, and kept).
+int scratch_address(int dev, void** out) {
+    static std::mutex mu;
+    static void* addr[64];
+    if (dev < 0 || dev >= 64) return fail(MOE_NVFP4_ERR_HIP, "device id %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(MOE_NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return MOE_NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -360,6 +386,26 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     if ((st = hip_status(moe::launch_combine(c, s), "combine launch"))) return st;
     if ((st = mark(5))) return st;
     return ok();
+}
+
+int moe_nvfp4_forward_noalloc(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w,
+                              const moe_nvfp4_weights* local, const moe_nvfp4_weights* shared, void* out,
+                              void* stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    Plan pl;
+    make_plan(*p, pl);
+    if (pl.total > kNoAllocScratchBytes)
+        return fail(MOE_NVFP4_ERR_WORKSPACE_TOO_SMALL,
+                    "this problem needs %zu bytes of scratch; the no-allocation forward holds %zu "
+                    "(use moe_nvfp4_forward with a workspace)",
+                    pl.total, kNoAllocScratchBytes);
+    int dev;
+    if ((st = current_arch_ok(&dev))) return st;
+    void* ws = nullptr;
+    if ((st = scratch_address(dev, &ws))) return st;
+    return moe_nvfp4_forward_timed(p, hidden, gate_w, local, shared, ws, kNoAllocScratchBytes, out, stream,
+                                   nullptr, 0);
 }
 
 int moe_nvfp4_route(const moe_nvfp4_problem* p, const void* hidden, const void* gate_w, int32_t* topk_ids,
