@@ -8,14 +8,20 @@ permutation, [W4A4 activation quantizer], GEMM1 + SwiGLU, GEMM2, weighted
 combine with the shared expert) over one batch of synthetic tokens whose
 weights and inputs are already resident in HBM.  Prints ONE JSON line for the
 headline workload (the T=64 expert-shard decode step), with:
-  value      tokens/s of the whole job (T * K / elapsed, wall clock around K steps)
-  roofline   the dominant kernel against its roof (HBM for decode, bf16 MFMA for
-             prefill): algorithmic bytes (or flops) per launch / the kernel's
-             average duration from the two HIP events recorded around it in each
-             timed step (the per-stage breakdown comes from a separate pass)
+  value      tokens/s of the whole job (T * K / elapsed, wall clock around
+             exactly K steps, synchronized on both sides; before the W warm-up
+             steps, ~0.3 s of untimed calls let the GPU clocks settle)
+  per_call_us  median and min of single calls (HIP events between consecutive
+             calls: N = 200 for the decode/shard workloads, 20 for prefill)
+  roofline   the dominant kernel (GEMM1 + SwiGLU) against its roof (HBM for
+             weight streaming, the 16-bit MFMA peak for tiles): algorithmic
+             bytes (or flops) per launch / its average duration from HIP events
+             recorded around it in the timed steps, on the kernels' stream
   graph_replay  the same forward captured once in a HIP graph, K replays timed
-  secondary  the same for the T=8192 all-expert W4A4 prefill step
-  cpu_baseline  the CPU oracle timed on a bounded sample of the headline workload
+  cpu_baseline  the CPU oracle timed on a bounded sample of the workload
+  secondary  the same measurements for the other four workloads (tiny layer,
+             T=512 W4A4 second shard, T=8192 all-expert W4A4 prefill, T=16384
+             Zipf-skewed W4A16 shard), each with its own roofline and oracle
 --all prints one line per workload instead (a report, not the default line).
 """
 import argparse
@@ -40,12 +46,21 @@ METRIC = "NVFP4 MoE layer tokens/s; % of HBM roofline (T=64), % MFMA peak (T=819
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 HEADLINE = "decode_shard0_w4a16"
-SECONDARY = "prefill_all_w4a4"
+SECONDARY = ["tiny_w4a16", "shard1_w4a4_t512", "prefill_all_w4a4", "prefill_zipf_shard0_w4a16"]
+# per-call timing sample sizes (median and min are reported)
+PER_CALL_N = {"tiny_w4a16": 200, "decode_shard0_w4a16": 200, "shard1_w4a4_t512": 200,
+              "shard1_w4a4_static_t512": 200, "prefill_all_w4a4": 20, "prefill_zipf_shard0_w4a16": 20}
+# tokens of each workload the CPU oracle is timed on (a bounded sample, ~3-15 s
+# of host time each; the tiny layer whole, repeated)
+CPU_SAMPLE = {"tiny_w4a16": 16, "decode_shard0_w4a16": 24, "shard1_w4a4_t512": 24,
+              "shard1_w4a4_static_t512": 24, "prefill_all_w4a4": 16, "prefill_zipf_shard0_w4a16": 32}
 STAGES = ["route_permute", "act_quant", "gemm1_swiglu", "gemm2", "combine"]
 G1_EVERY = 4                    # timed steps per GEMM1 event pair
+PREWARM_S = 0.3                 # untimed forward calls before the warm-up steps (clock settling)
 CSRC = os.path.join(ROOT, "nvfp4_expert_layer_amd", "csrc")
 # sources whose machine code the dominant kernel of each path is built from
 KERNEL_SOURCES = {"decode": ["decode.hip", "device_common.h", "kernels.h"],
+                  "mid": ["mid.hip", "device_common.h", "kernels.h"],
                   "prefill": ["prefill.hip", "device_common.h", "kernels.h"]}
 
 
@@ -114,6 +129,7 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -123,6 +139,11 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             out.append(e.value)
         return out
+
+    def record(self, e):
+        """Record event e on torch's current stream (the stream the forward runs on)."""
+        if self.lib.hipEventRecord(e, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -181,6 +202,16 @@ def bench_workload(name, steps, warmup, hip):
     p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode, nv.PATH_AUTO, w.act_global)
     ws = nv.alloc_workspace(p)
     out = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
+    # pre-warm (untimed): the GPU's clocks need ~0.1-0.2 s of load to settle; at
+    # T=64 twenty steps right after set-up measured 409 us/step, 222 after 20
+    # more, 217 after 200 (the per-call median is the same in each)
+    t_end = time.perf_counter() + PREWARM_S
+    prewarm_calls = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+        prewarm_calls += 10
+        torch.cuda.synchronize()
     for _ in range(warmup):
         nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
     # timed region: K steps.  The dominant kernel's duration is measured live:
@@ -216,6 +247,21 @@ def bench_workload(name, steps, warmup, hip):
     torch.cuda.synchronize()
     graph_s = time.perf_counter() - tg
     del graph
+    # single calls: an event between consecutive calls (N of them), median and min
+    n_calls = max(PER_CALL_N.get(name, 20), steps)
+    cev = hip.create(n_calls + 1)
+    hip.record(cev[0])
+    for i in range(n_calls):
+        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+        hip.record(cev[i + 1])
+    torch.cuda.synchronize()
+    call_us = sorted(hip.elapsed_ms(cev[i], cev[i + 1]) * 1e3 for i in range(n_calls))
+    hip.destroy(cev)
+    per_call = {"median": round(call_us[n_calls // 2] if n_calls % 2 else
+                                0.5 * (call_us[n_calls // 2 - 1] + call_us[n_calls // 2]), 2),
+                "min": round(call_us[0], 2), "n": n_calls,
+                "tokens_per_s_at_median": None}
+    per_call["tokens_per_s_at_median"] = round(w.T / (per_call["median"] * 1e-6), 1)
     # per-stage breakdown from a separate, untimed pass with all six events
     nb = min(steps, 10)
     evs = hip.create(6 * nb)
@@ -233,7 +279,7 @@ def bench_workload(name, steps, warmup, hip):
     torch.cuda.synchronize()
     alg = algorithmic(w, counts.cpu())
     ms = elapsed * 1e3 / steps
-    path = "decode" if nv.moe_nvfp4_resolved_path(p) == nv.PATH_DECODE else "prefill"
+    path = {nv.PATH_DECODE: "decode", nv.PATH_MID: "mid", nv.PATH_PREFILL: "prefill"}[nv.moe_nvfp4_resolved_path(p)]
     g1_s = g1_ms * 1e-3
     # the binding roofline of GEMM1 is the one its algorithmic bytes or flops
     # come closer to (HBM for weight streaming, the 16-bit MFMA peak for tiles)
@@ -252,60 +298,69 @@ def bench_workload(name, steps, warmup, hip):
     layer_hbm_frac = alg["layer_bytes"] / (HBM_PEAK_GBS * 1e9) / (ms * 1e-3)
     layer_mfma_frac = alg["layer_flops"] / (BF16_PEAK_TFLOPS * 1e12) / (ms * 1e-3)
     res = {"workload": name, "tokens_per_s": w.T * steps / elapsed, "ms_per_step": ms,
+           "prewarm": {"seconds": PREWARM_S, "calls": prewarm_calls},
            "graph_tokens_per_s": w.T * steps / graph_s, "graph_ms_per_step": graph_s * 1e3 / steps,
            "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
-           "roofline": roof, "layer_hbm_frac": round(layer_hbm_frac, 4),
+           "roofline": roof, "per_call_us": per_call, "layer_hbm_frac": round(layer_hbm_frac, 4),
            "layer_mfma_frac": round(layer_mfma_frac, 4),
            "touched_experts": alg["touched"], "local_pairs": alg["P"],
-           # the type the GEMMs multiply in: W4A4 on the tiled path multiplies
-           # exact NVFP4 products in f16, everything else in bf16
-           "dtype": "f16" if (path == "prefill" and w.mode != workloads.W4A16) else "bf16"}
+           # the type the GEMMs multiply in: W4A4 on the tiled and dense
+           # weight-streaming paths multiplies exact NVFP4 products in f16,
+           # everything else in bf16
+           "dtype": "f16" if (path != "decode" and w.mode != workloads.W4A16) else "bf16"}
     del local, shared, ws
     torch.cuda.empty_cache()
     return w, res
 
 
-def _cpu_expert(args):
-    wdict, e = args
-    import workloads as wl
-    from tests.oracle_helpers import quantize_expert_oracle
-    w = wl.Workload(**wdict)
-    w13, w2 = wl.gen_expert(w, e, "cpu")
-    return e, quantize_expert_oracle(w13, w2)
-
-
-def cpu_baseline(name, sample_tokens):
-    """The oracle (numpy fp64) on the first `sample_tokens` tokens of the
-    workload; weights drawn on the CPU and quantized by the oracle (untimed)."""
-    from concurrent.futures import ProcessPoolExecutor
-    import multiprocessing as mp
-    # runs before anything touches the GPU; workers are fresh interpreters (spawn)
-
+def cpu_baselines(names):
+    """The oracle (numpy fp64, as it stands: experts one after another, BLAS on
+    all host cores it may use) timed on the first CPU_SAMPLE[name] tokens of each
+    workload; the weights those tokens touch are drawn on the CPU and quantized
+    by the oracle on a process pool beforehand (untimed).  Runs before anything
+    touches the GPU."""
+    import numpy as np
     from oracle import moe
+    from tests import oracle_pool
     from tests.oracle_helpers import to_f64
-    w = workloads.WORKLOADS[name]
-    x = to_f64(workloads.gen_hidden(w, "cpu", T=sample_tokens))
-    G = to_f64(workloads.gen_gate(w, "cpu"))
-    ids = moe.route(x, G, w.k)["ids"]
-    need = sorted({int(e) for e in ids.reshape(-1) if w.offset <= e < w.offset + w.L})
-    if w.has_shared:
-        need.append(w.E)
-    wdict = {k: getattr(w, k) for k in w.__dataclass_fields__}
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
-        q = dict(ex.map(_cpu_expert, [(wdict, e) for e in need]))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
-    t0 = time.perf_counter()
-    moe.forward(x, G, lambda l: q[w.offset + l], q.get(w.E), w.k, w.offset, w.L, w.mode, act_global=w.act_global)
-    dt = time.perf_counter() - t0
-    return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample_tokens} of {w.T} tokens of {name} ({len(need)} experts touched); "
-                      f"numpy fp64, BLAS threads {threads}, host cores {len(os.sched_getaffinity(0))}; "
-                      f"{dt:.1f} s"}
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    cache = {}
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        n = min(CPU_SAMPLE.get(name, 16), w.T)
+        x = to_f64(workloads.gen_hidden(w, "cpu", T=n))
+        G = to_f64(workloads.gen_gate(w, "cpu"))
+        ids = moe.route(x, G, w.k)["ids"].reshape(-1)
+        need = sorted({int(e) for e in ids if w.offset <= e < w.offset + w.L})
+        if w.has_shared:
+            need.append(w.E)
+        key = lambda e: (w.weight_seed, w.d, w.F, w.E, e)
+        todo = [e for e in need if key(e) not in cache]
+        jobs = []
+        for e in todo:
+            w13, w2 = workloads.gen_expert(w, e, "cpu")
+            jobs.append((w13.view(torch.int16).numpy().view(np.uint16), w2.view(torch.int16).numpy().view(np.uint16)))
+        for e, q in zip(todo, oracle_pool.pool_map(oracle_pool.quantize_expert_bits, jobs)):
+            cache[key(e)] = q
+        reps, dt = 0, 0.0
+        while reps == 0 or dt < 1.0:          # the tiny layer is repeated to >= 1 s
+            t0 = time.perf_counter()
+            moe.forward(x, G, lambda l: cache[key(w.offset + l)], cache.get(key(w.E)), w.k, w.offset, w.L,
+                        w.mode, act_global=w.act_global)
+            dt += time.perf_counter() - t0
+            reps += 1
+        res[name] = {"value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                     "sample": f"first {n} of {w.T} tokens of {name} ({len(need)} experts touched"
+                               f"{', x%d' % reps if reps > 1 else ''}); numpy fp64, BLAS threads {threads}, "
+                               f"host cores {cores}; {dt:.1f} s"}
+    oracle_pool.pool().shutdown()
+    return res
 
 
 def config_of(w):
@@ -317,6 +372,19 @@ def config_of(w):
     return c
 
 
+def summary(w, r, cpu):
+    """The measurements of one workload (a secondary entry)."""
+    d = {"config": config_of(w), "dtype": r["dtype"], "tokens_per_s": round(r["tokens_per_s"], 1),
+         "ms_per_step": round(r["ms_per_step"], 4), "per_call_us": r["per_call_us"], "roofline": r["roofline"],
+         "graph_replay": {"tokens_per_s": round(r["graph_tokens_per_s"], 1),
+                          "ms_per_step": round(r["graph_ms_per_step"], 4)},
+         "layer_hbm_frac": r["layer_hbm_frac"], "layer_mfma_frac": r["layer_mfma_frac"],
+         "stage_us": r["stage_us"], "touched_experts": r["touched_experts"], "local_pairs": r["local_pairs"]}
+    if cpu is not None:
+        d["cpu_baseline"] = cpu
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,8 +394,6 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=48,
-                    help="tokens of the headline batch the CPU oracle is timed on (~10-30 s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hashes and exit")
@@ -339,11 +405,12 @@ def main():
         print(json.dumps({"error": "this layer runs on one GPU: the expert shard is exercised by running one "
                                    "shard's experts locally; --gpus must be 1"}))
         sys.exit(2)
-    names = list(workloads.WORKLOADS) if args.all else [args.workload]
-    # the CPU oracle baseline first, before the process initialises the GPU
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload if not args.all else HEADLINE, args.cpu_sample)
+    if args.all:
+        names = list(workloads.WORKLOADS)
+    else:
+        names = [args.workload] + ([] if args.no_secondary else [n for n in SECONDARY if n != args.workload])
+    # the CPU oracle baselines first, before the process initialises the GPU
+    cpu = {} if args.no_cpu_baseline or args.copy_calibration else cpu_baselines(names)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -351,27 +418,33 @@ def main():
         return
     nv.lib()
     hip = HipEvents()
-    for name in names:
-        w, r = bench_workload(name, args.steps, args.warmup, hip)
+    results = []
+    for i, name in enumerate(names):
+        # the secondary prefill workloads take fewer timed steps (each is ~10x longer)
+        steps = args.steps if (i == 0 or args.all or PER_CALL_N.get(name, 20) >= 200) else max(5, args.steps // 2)
+        results.append((name, steps) + bench_workload(name, steps, args.warmup, hip))
+    lines = []
+    for j, (name, steps, w, r) in enumerate(results):
         line = {"metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
-                "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
+                "steps": steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4),
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": r["dtype"],
                 "data": "synthetic (seeded bf16 draws, NVFP4-quantized on the GPU)", "config": config_of(w),
-                "roofline": r["roofline"], "graph_replay": {"tokens_per_s": round(r["graph_tokens_per_s"], 1),
-                                                            "ms_per_step": round(r["graph_ms_per_step"], 4)},
+                "roofline": r["roofline"], "per_call_us": r["per_call_us"],
+                "graph_replay": {"tokens_per_s": round(r["graph_tokens_per_s"], 1),
+                                 "ms_per_step": round(r["graph_ms_per_step"], 4)},
                 "layer_hbm_frac": r["layer_hbm_frac"],
                 "layer_mfma_frac": r["layer_mfma_frac"], "stage_us": r["stage_us"],
-                "touched_experts": r["touched_experts"], "local_pairs": r["local_pairs"]}
-        if not args.all and not args.no_secondary and name != SECONDARY:
-            w2, r2 = bench_workload(SECONDARY, max(5, args.steps // 5), args.warmup, hip)
-            line["secondary"] = {"config": config_of(w2), "dtype": r2["dtype"],
-                                 "tokens_per_s": round(r2["tokens_per_s"], 1),
-                                 "ms_per_step": round(r2["ms_per_step"], 4), "roofline": r2["roofline"],
-                                 "graph_replay": {"tokens_per_s": round(r2["graph_tokens_per_s"], 1),
-                                                  "ms_per_step": round(r2["graph_ms_per_step"], 4)},
-                                 "layer_mfma_frac": r2["layer_mfma_frac"], "stage_us": r2["stage_us"]}
-        if cpu is not None and (not args.all or name == HEADLINE):
-            line["cpu_baseline"] = cpu
+                "touched_experts": r["touched_experts"], "local_pairs": r["local_pairs"],
+                "prewarm": r["prewarm"]}
+        if name in cpu:
+            line["cpu_baseline"] = cpu[name]
+        if args.all:
+            lines.append(line)
+            continue
+        line["secondary"] = [summary(w2, r2, cpu.get(n2)) for n2, _, w2, r2 in results[1:]]
+        lines.append(line)
+        break
+    for line in lines:
         print(json.dumps(line), flush=True)
 
 

@@ -117,8 +117,10 @@ typedef enum {
  * other. */
 typedef enum {
     MOE_NVFP4_PATH_AUTO = 0,
-    MOE_NVFP4_PATH_DECODE = 1,
-    MOE_NVFP4_PATH_PREFILL = 2
+    MOE_NVFP4_PATH_DECODE = 1,   /* weight streaming, block-diagonal MFMA, 4-16-row tiles */
+    MOE_NVFP4_PATH_PREFILL = 2,  /* 256 x 256 MFMA tiles                                  */
+    MOE_NVFP4_PATH_MID = 3       /* weight streaming, dense MFMA, 32-row tiles; needs
+                                    d_model % 256 == 0 (else UNSUPPORTED_SHAPE)          */
 } moe_nvfp4_path;
 
 typedef struct {

@@ -51,14 +51,26 @@ bool is_w4a4(int mode) { return mode == MOE_NVFP4_W4A4 || mode == MOE_NVFP4_W4A4
 
 // Path actually used for a problem (AUTO resolved by the expected local load).
 int resolve_path(const moe_nvfp4_problem& p) {
-    if (p.path == MOE_NVFP4_PATH_DECODE || p.path == MOE_NVFP4_PATH_PREFILL) return p.path;
+    if (p.path != MOE_NVFP4_PATH_AUTO) return p.path;
     // expected local pairs per local expert: T * k / E (uniform routing).  The
-    // crossover was measured on the 4096 x 1024 layer with 160 local experts:
-    // the tiled kernels stay near-flat in T while weight streaming grows with
-    // the rows per expert; packed W4A4 tiles move 3.5x fewer activation bytes
-    // and cross earlier.
+    // crossovers were measured on the 4096 x 1024 layer with 160 local experts
+    // (per-call medians):
+    //   W4A16: weight streaming with the block-diagonal kernels up to ~5.5 pairs
+    //   per expert (T = 192: 345 us against 355 dense), the dense
+    //   weight-streaming kernels up to ~22 (T = 384: 384 us against 539
+    //   block-diagonal and 552 tiled; T = 768: 575 against 627 tiled), then the
+    //   tiles (T = 1024: 621 against 650);
+    //   packed W4A4 (tiles moving NVFP4 activations, 3.5x fewer bytes): weight
+    //   streaming up to 6, tiles above (the dense kernels measured a few per
+    //   cent slower there: T = 512: 388 against 371 us);
+    //   W4A4 whose d or F rules out packed tiles: weight streaming up to 9.
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
-    const bool packed = is_w4a4(p.mode) && moe::pf_packed_ok(p.d_model, p.d_ff);
+    const bool w4a4 = is_w4a4(p.mode);
+    const bool packed = w4a4 && moe::pf_packed_ok(p.d_model, p.d_ff);
+    if (!w4a4 && moe::mid_ok(p.d_model, p.d_ff)) {
+        if (per_expert <= 5.5) return MOE_NVFP4_PATH_DECODE;
+        return per_expert <= 22.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
+    }
     return per_expert <= (packed ? 6.0 : 9.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
 }
 
@@ -77,7 +89,7 @@ int check_problem(const moe_nvfp4_problem* p) {
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown mode %d", p->mode);
     if (p->mode == MOE_NVFP4_W4A4_STATIC && (!global_ok(p->act_global13) || !global_ok(p->act_global2)))
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "static W4A4 activation globals must be finite, in 2^-100..2^100");
-    if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_PREFILL)
+    if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_MID)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown path %d", p->path);
     if (p->has_shared != 0 && p->has_shared != 1)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "has_shared must be 0 or 1");
@@ -94,6 +106,8 @@ int check_problem(const moe_nvfp4_problem* p) {
                     p->d_model);
     if (p->d_ff < 128 || p->d_ff > 16384 || p->d_ff % 128)
         return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_ff %d: need a multiple of 128 in 128..16384", p->d_ff);
+    if (p->path == MOE_NVFP4_PATH_MID && !moe::mid_ok(p->d_model, p->d_ff))
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "the dense weight-streaming path needs d_model %% 256 == 0");
     // index arithmetic: pair rows and per-row offsets stay within int32
     const long long rows = (long long)p->num_tokens * (p->top_k + 1);
     if (rows > (1LL << 27)) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "num_tokens * (top_k + 1) > 2^27");
@@ -106,7 +120,7 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.exact = moe::router_exact((int)T, (int)E, (int)d);
     pl.KS = pl.exact ? moe::router_exact_ksplit((int)T, (int)E, (int)d) : moe::router_ksplit((int)T, (int)E, (int)d);
     pl.path = resolve_path(p);
-    pl.BM = moe::gemm_bm(pl.path, (int)T, (int)k, (int)E);
+    pl.BM = moe::gemm_bm(pl.path, (int)T, (int)k, (int)E, is_w4a4(p.mode) && moe::mid_packed_ok((int)d, (int)F));
     const size_t bm = pl.BM;
     pl.max_tiles = (int)((T * k + bm - 1) / bm + L + (p.has_shared ? (T + bm - 1) / bm : 0));
     pl.nblk = (int)((T + 255) / 256);
@@ -330,9 +344,11 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     const bool stat = p->mode == MOE_NVFP4_W4A4_STATIC;
     const float a1g = stat ? p->act_global13 : 1.0f, a2g = stat ? p->act_global2 : 1.0f;
     const bool tiled = pl.path == MOE_NVFP4_PATH_PREFILL;
+    const bool mid = pl.path == MOE_NVFP4_PATH_MID;
     // W4A4 on the tiled path: the activations travel as NVFP4 codes and scales
     // when d and F allow it, else as exact f16 values
-    const bool packed = w4a4 && tiled && moe::pf_packed_ok(p->d_model, p->d_ff);
+    const bool packed = w4a4 && ((tiled && moe::pf_packed_ok(p->d_model, p->d_ff)) ||
+                                 (mid && moe::mid_packed_ok(p->d_model, p->d_ff)));
     uint8_t* hq_codes = at<uint8_t>(workspace, pl.hq);
     uint8_t* hq_scales = hq_codes + (size_t)p->num_tokens * (p->d_model / 2);
     uint8_t* act_codes = at<uint8_t>(workspace, pl.act);
@@ -344,7 +360,8 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
                             "activation quantizer launch");
         else
             st = hip_status(moe::launch_fake_quant_act(static_cast<const uint16_t*>(hidden), p->num_tokens,
-                                                       p->d_model, a1g, at<uint16_t>(workspace, pl.hq), tiled, s),
+                                                       p->d_model, a1g, at<uint16_t>(workspace, pl.hq),
+                                                       tiled || mid, s),
                             "activation quantizer launch");
         if (st) return st;
     }
@@ -371,10 +388,14 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
     g.act_codes = act_codes;
     g.act_scales = act_scales;
     const bool dec = pl.path == MOE_NVFP4_PATH_DECODE;
-    if ((st = hip_status(dec ? moe::launch_dec_gemm1(g, s) : moe::launch_gemm1(g, pl.path, s), "gemm1 launch")))
+    if ((st = hip_status(dec ? moe::launch_dec_gemm1(g, s)
+                             : (mid ? moe::launch_mid_gemm1(g, s) : moe::launch_gemm1(g, pl.path, s)),
+                         "gemm1 launch")))
         return st;
     if ((st = mark(3))) return st;
-    if ((st = hip_status(dec ? moe::launch_dec_gemm2(g, s) : moe::launch_gemm2(g, pl.path, s), "gemm2 launch")))
+    if ((st = hip_status(dec ? moe::launch_dec_gemm2(g, s)
+                             : (mid ? moe::launch_mid_gemm2(g, s) : moe::launch_gemm2(g, pl.path, s)),
+                         "gemm2 launch")))
         return st;
     if ((st = mark(4))) return st;
     moe::CombineArgs c{};

@@ -52,12 +52,13 @@ struct GemmArgs {
     int max_tiles;
     const uint16_t* hidden;       // bf16 [T][d]
     const uint16_t* hq;           // W4A4: hidden NVFP4-quantized, exact dequantized [T][d]
-                                  //   (bf16 on the decode path, f16 on the tiled path)
+                                  //   (bf16 on the decode path, f16 on the tiled and mid paths)
     ExpertWeights local, shared;
     uint16_t* act;                // SwiGLU output [R][F]: bf16; W4A4: exact dequantized NVFP4
-                                  //   values, bf16 (decode path) or f16 (tiled path)
+                                  //   values, bf16 (decode path) or f16 (tiled and mid paths)
     uint16_t* Y;                  // expert outputs, bf16 [R][d];  R = T*k + T
-    // W4A4 on the tiled path when d and F are multiples of 256 (packed != 0):
+    // W4A4 on the tiled path when d and F are multiples of 256, and on the dense
+    // weight-streaming path when they are also at most 8192 (packed != 0):
     // activations travel as NVFP4 codes and E4M3 block scales instead of 16-bit
     // values (in the hq and act regions)
     int packed;
@@ -91,7 +92,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_prepare_rows(const uint8_t* src, uint8_t* dst, int n, int rows, int row_bytes, bool swap_halves,
                                hipStream_t s);
 hipError_t launch_prepare_global(const float* src, float* dst, int n, bool inverse, hipStream_t s);
-int gemm_bm(int path, int T, int topk, int E);   // rows per tile of the chosen path
+int gemm_bm(int path, int T, int topk, int E, bool packed_mid);   // rows per tile of the chosen path
 int pf_rows();                                    // rows per tile of the prefill GEMMs
 bool pf_packed_ok(int d, int F);                  // W4A4 packed-activation GEMMs apply
 int dec_rows(int T, int topk, int E);
@@ -100,6 +101,12 @@ hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s);
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+bool mid_ok(int d, int F);                        // dense weight-streaming kernels apply
+bool mid_packed_ok(int d, int F);                 // ... with W4A4 activations as NVFP4
+int mid_rows();                                   // rows per tile of the dense weight-streaming path
+int mid_rows_packed();                            // ... with W4A4 activations as NVFP4
+hipError_t launch_mid_gemm1(const GemmArgs& a, hipStream_t s);
+hipError_t launch_mid_gemm2(const GemmArgs& a, hipStream_t s);
 
 // Raise kernel Kern's dynamic-LDS limit to `bytes` on the current device when
 // that is above the 64 KB default; the attribute is per device, so the largest

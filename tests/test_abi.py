@@ -91,18 +91,25 @@ def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
 
 
 def test_resolved_path_crossover():
-    # expected local pairs per local expert T*k/E: weight streaming up to 9
-    # (W4A16, or W4A4 whose d or F is not a multiple of 256), 6 for packed W4A4
+    # expected local pairs per local expert T*k/E: W4A16 streams with the
+    # block-diagonal kernels up to 5.5, with the dense ones up to 22 (d % 256
+    # == 0), then tiles; packed W4A4 streams up to 6; W4A4 whose d or F is not
+    # a multiple of 256 streams up to 9
     def path(T, mode, d=4096, F=1024, force=nv.PATH_AUTO):
         return nv.moe_nvfp4_resolved_path(nv.make_problem(T, d, F, 320, 8, 0, 160, True, mode, force))
     assert path(64, nv.W4A16) == nv.PATH_DECODE
-    assert path(360, nv.W4A16) == nv.PATH_DECODE          # 9.0
-    assert path(361, nv.W4A16) == nv.PATH_PREFILL
+    assert path(220, nv.W4A16) == nv.PATH_DECODE          # 5.5
+    assert path(221, nv.W4A16) == nv.PATH_MID
+    assert path(880, nv.W4A16) == nv.PATH_MID             # 22.0
+    assert path(881, nv.W4A16) == nv.PATH_PREFILL
+    assert path(360, nv.W4A16, d=3968) == nv.PATH_DECODE  # d % 256 != 0: no dense path, threshold 9
+    assert path(361, nv.W4A16, d=3968) == nv.PATH_PREFILL
     assert path(240, nv.W4A4) == nv.PATH_DECODE           # 6.0
     assert path(241, nv.W4A4) == nv.PATH_PREFILL
     assert path(300, nv.W4A4, F=384) == nv.PATH_DECODE    # not packed: threshold 9
     assert path(8192, nv.W4A16, force=nv.PATH_DECODE) == nv.PATH_DECODE
     assert path(1, nv.W4A4, force=nv.PATH_PREFILL) == nv.PATH_PREFILL
+    assert path(1, nv.W4A4, force=nv.PATH_MID) == nv.PATH_MID
     with pytest.raises(nv.MoeNvfp4Error):
         path(64, nv.W4A16, d=100)
 
@@ -123,3 +130,13 @@ def test_static_globals_are_validated():
     pd = nv.make_problem(300, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4)
     assert nv.moe_nvfp4_resolved_path(ps) == nv.moe_nvfp4_resolved_path(pd) == nv.PATH_PREFILL
     assert nv.moe_nvfp4_workspace_size(ps) == nv.moe_nvfp4_workspace_size(pd)
+
+
+def test_mid_path_needs_d_multiple_of_256():
+    p = nv.make_problem(64, 384, 256, 16, 2, 0, 16, True, nv.W4A16, nv.PATH_MID)
+    assert nv.moe_nvfp4_validate(p, 1 << 30, None) == nv.ERR_UNSUPPORTED_SHAPE
+    p = nv.make_problem(64, 512, 256, 16, 2, 0, 16, True, nv.W4A16, nv.PATH_MID)
+    assert nv.moe_nvfp4_validate(p, 1 << 30, None) == nv.OK
+    assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_MID
+    bad = nv.make_problem(64, 512, 256, 16, 2, 0, 16, True, nv.W4A16, 4)
+    assert nv.moe_nvfp4_validate(bad, 1 << 30, None) == nv.ERR_INVALID_ARG

@@ -18,7 +18,7 @@ from tests.oracle_helpers import to_f64
 pytestmark = pytest.mark.gpu
 
 W4A16, W4A4 = workloads.W4A16, workloads.W4A4
-PATHS = [nv.PATH_DECODE, nv.PATH_PREFILL]
+PATHS = [nv.PATH_DECODE, nv.PATH_PREFILL, nv.PATH_MID]
 
 _layers = {}
 
@@ -73,7 +73,7 @@ def test_mid_layer_full_output(mode, path, offset, L, shared):
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
-@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
 @pytest.mark.parametrize("offset,L,shared", [(0, 5, True), (1, 3, False)])
 def test_wide_layer_full_output(mode, path, offset, L, shared):
     require_gpu()
@@ -175,11 +175,11 @@ def full_layer(name):
     return lay
 
 
-def whole_output_check(lay, offset, L, has_shared, mode, what):
+def whole_output_check(lay, offset, L, has_shared, mode, what, path=nv.PATH_AUTO):
     """GPU forward against the oracle's whole output; logs the error, the
     routing ambiguity count and the worst token row's error."""
     w = lay.w
-    out = lay.run(offset, L, has_shared, mode)
+    out = lay.run(offset, L, has_shared, mode, path)
     assert not torch.isnan(out).any().item()
     ref = lay.oracle_full(offset, L, has_shared, mode)
     err = rel_err(out, ref["out"])
@@ -225,8 +225,8 @@ def test_decode_tile_heights(T, mode):
 
 
 @pytest.mark.parametrize("T", [32, 128, 240, 360])
-def test_full_size_decode_other_token_counts(T):
-    """The 320-expert shard on weight streaming at T = 32 (two row groups per
+def test_full_size_decode_other_token_counts(T):  # forced onto the block-diagonal path
+    """The 320-expert shard on block-diagonal weight streaming at T = 32 (two row groups per
     wave in GEMM1), 128 (4-row tiles at 4 pairs per expert), 240 (6 pairs per
     expert: the down projection merges two 4-row tiles) and 360 (8-row tiles,
     whose whole-K token stage of 65.7 KB takes more than 64 KB of LDS); the
@@ -237,10 +237,8 @@ def test_full_size_decode_other_token_counts(T):
     w = workloads.replace(base, T=T, hidden_seed=base.hidden_seed + T)
     lay.w = w
     lay.x = workloads.gen_hidden(w, "cuda")
-    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode)
-    assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_DECODE
     log(f"full-size decode T={T}")
-    whole_output_check(lay, w.offset, w.L, w.has_shared, w.mode, f"decode T={T}")
+    whole_output_check(lay, w.offset, w.L, w.has_shared, w.mode, f"decode T={T}", nv.PATH_DECODE)
 
 
 def test_full_size_two_shards_sum_to_unsharded_oracle():
@@ -258,3 +256,47 @@ def test_full_size_two_shards_sum_to_unsharded_oracle():
     err = moe.normwise_rel_err(s.cpu().numpy(), full)
     log(f"two shards vs unsharded oracle, whole output: {err:.3e}")
     assert err <= tol(W4A4)
+
+
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 200])
+def test_mid_path_tile_edges(T, mode):
+    """The dense weight-streaming path on 16-row tiles: one token, one short of
+    a tile, exactly a tile, one past it (an expert with two tiles), and many
+    tiles per expert; whole output."""
+    require_gpu()
+    lay = layer("mid", T=T)
+    w = lay.w
+    log(f"mid path T={T} mode={mode}")
+    out = lay.run(w.offset, w.L, w.has_shared, mode, nv.PATH_MID)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, mode)
+    err = rel_err(out, ref["out"])
+    log(f"  normwise rel err {err:.3e}")
+    assert err <= tol(mode)
+
+
+@pytest.mark.parametrize("name", ["shard1_w4a4_t512", "decode_shard0_w4a16"])
+def test_full_size_mid_path(name):
+    """The full-size shards through the dense weight-streaming path (whatever
+    AUTO picks for them), whole output against the oracle."""
+    require_gpu()
+    lay = full_layer(name)
+    w = lay.w
+    log(f"full-size {name} on the mid path")
+    whole_output_check(lay, w.offset, w.L, w.has_shared, w.mode, f"{name} mid path", nv.PATH_MID)
+
+
+@pytest.mark.parametrize("T", [384, 880])
+def test_full_size_mid_path_auto(T):
+    """The 320-expert W4A16 shard where AUTO picks the dense weight-streaming
+    path (9.6 and 22 pairs per expert), whole output."""
+    require_gpu()
+    base = workloads.WORKLOADS["decode_shard0_w4a16"]
+    lay = full_layer("decode_shard0_w4a16")
+    w = workloads.replace(base, T=T, hidden_seed=base.hidden_seed + T)
+    lay.w = w
+    lay.x = workloads.gen_hidden(w, "cuda")
+    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode)
+    assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_MID
+    log(f"full-size mid (AUTO) T={T}")
+    whole_output_check(lay, w.offset, w.L, w.has_shared, w.mode, f"mid T={T}")

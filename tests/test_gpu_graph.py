@@ -54,7 +54,7 @@ def _graph_vs_eager(lay, offset, L, shared, mode, path, n_replays=3):
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
-@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL])
+@pytest.mark.parametrize("path", [nv.PATH_DECODE, nv.PATH_PREFILL, nv.PATH_MID])
 def test_graph_replays_match_eager_mid(mode, path):
     require_gpu()
     lay = Layer(MID)
@@ -62,12 +62,14 @@ def test_graph_replays_match_eager_mid(mode, path):
     _graph_vs_eager(lay, 4, 16, True, mode, path)
 
 
-@pytest.mark.parametrize("T", [64, 256])
-def test_graph_replays_match_eager_decode_shard(T):
-    """T = 64: exact routing, 4-row weight-streaming tiles; T = 256: certified
-    routing, one-workgroup permutation, 8-row tiles with more than 64 KB of LDS."""
+@pytest.mark.parametrize("T,path", [(64, nv.PATH_AUTO), (256, nv.PATH_DECODE), (384, nv.PATH_AUTO)])
+def test_graph_replays_match_eager_decode_shard(T, path):
+    """T = 64: exact routing, 4-row weight-streaming tiles; T = 256 (block-
+    diagonal path forced): certified routing, one-workgroup permutation, 8-row
+    tiles with more than 64 KB of LDS; T = 384: the dense weight-streaming path
+    AUTO picks there."""
     require_gpu()
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     lay = Layer(w, experts_range=(0, w.L))
-    log(f"graph replay decode shard T={T}")
-    _graph_vs_eager(lay, w.offset, w.L, True, w.mode, nv.PATH_AUTO)
+    log(f"graph replay decode shard T={T} path={path}")
+    _graph_vs_eager(lay, w.offset, w.L, True, w.mode, path)

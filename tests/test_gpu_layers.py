@@ -18,7 +18,7 @@ W4A16, W4A4, STATIC = workloads.W4A16, workloads.W4A4, workloads.W4A4_STATIC
 
 
 def stack():
-    """Twelve small layers: three shapes, all modes, both kernel paths."""
+    """Twelve small layers: three shapes, all modes, every kernel path."""
     out = []
     shapes = [(96, 512, 256, 24, 4), (40, 256, 384, 16, 2), (300, 512, 512, 8, 2)]
     for i in range(12):
@@ -28,7 +28,7 @@ def stack():
                                has_shared=i % 2 == 0, mode=mode, hidden_seed=300 + i, gate_seed=300 + i,
                                weight_seed=300 + i, gate_std=0.05,
                                act_global=(0.0021, 0.0043) if mode == STATIC else (1.0, 1.0))
-        path = (nv.PATH_DECODE, nv.PATH_PREFILL, nv.PATH_AUTO)[i % 3]
+        path = (nv.PATH_DECODE, nv.PATH_PREFILL, nv.PATH_MID, nv.PATH_AUTO)[i % 4]
         out.append((Layer(w, experts_range=(w.offset, w.L)), path))
     return out
 
