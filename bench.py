@@ -78,6 +78,7 @@ def kernel_source_hash(path):
             t = "".join(re.findall(r"struct (?:ExpertWeights|GemmArgs) \{.*?\n\};", t, flags=re.S))
         t = re.sub(r"/\*.*?\*/", "", t, flags=re.S)          # comments do not change a kernel
         t = re.sub(r"//[^\n]*", "", t)
+        t = " ".join(t.split())                                # nor does layout
         h.update(t.encode())
     return h.hexdigest()[:16]
 
