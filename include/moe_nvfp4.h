@@ -119,8 +119,13 @@ typedef enum {
     MOE_NVFP4_PATH_AUTO = 0,
     MOE_NVFP4_PATH_DECODE = 1,   /* weight streaming, block-diagonal MFMA, 4-16-row tiles */
     MOE_NVFP4_PATH_PREFILL = 2,  /* 256 x 256 MFMA tiles                                  */
-    MOE_NVFP4_PATH_MID = 3       /* weight streaming, dense MFMA, 32-row tiles; needs
+    MOE_NVFP4_PATH_MID = 3,      /* weight streaming, dense MFMA, 16/32-row tiles; needs
                                     d_model % 256 == 0 (else UNSUPPORTED_SHAPE)          */
+    MOE_NVFP4_PATH_MICRO = 4     /* the whole layer in one persistent launch (one
+                                    workgroup per CU, grid barriers) for 1..16 tokens;
+                                    needs d_model, d_ff <= 4096, d_model % 256 == 0, and
+                                    the device otherwise idle for the launch's duration
+                                    (its barriers wait for every CU's workgroup)          */
 } moe_nvfp4_path;
 
 typedef struct {

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_nvfp4.so")
 W4A16 = 0
 W4A4 = 1
 W4A4_STATIC = 2
-PATH_AUTO, PATH_DECODE, PATH_PREFILL, PATH_MID = 0, 1, 2, 3
+PATH_AUTO, PATH_DECODE, PATH_PREFILL, PATH_MID, PATH_MICRO = 0, 1, 2, 3, 4
 
 OK = 0
 ERR_INVALID_ARG = 1
@@ -225,7 +225,7 @@ def moe_nvfp4_workspace_size(problem):
 
 
 def moe_nvfp4_resolved_path(problem):
-    """PATH_DECODE, PATH_MID or PATH_PREFILL: the path the forward takes for `problem`."""
+    """PATH_DECODE, PATH_MID, PATH_PREFILL or PATH_MICRO: the path the forward takes for `problem`."""
     out = ctypes.c_int32(0)
     _check(lib().moe_nvfp4_resolved_path(ctypes.byref(problem), ctypes.byref(out)))
     return out.value

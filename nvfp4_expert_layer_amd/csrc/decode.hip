@@ -30,6 +30,7 @@
 // 사항 › b12x에서의 Expert Parallelism 구현 추가" and "b12x 버전이 실제 NVFP4
 // 체크포인트를 읽어들이도록 만들기".
 #include <cmath>
+#include <type_traits>
 #include "device_common.h"
 #include "kernels.h"
 
@@ -75,12 +76,16 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     // ---- A stage: whole K once, or chunk 0 (the rest double-buffered below)
     constexpr int APT = ROWS * (kChunk / 8) / (64 * kDecWaves);   // 16-byte pieces per thread per chunk
     static_assert(APT * 64 * kDecWaves == ROWS * kChunk / 8, "A staging covers the chunk");
+    // loads are unconditional (a piece past the tile's rows or past K reads row 0
+    // or the row's last 16 bytes instead; only the stores are conditional): a
+    // load under a per-lane condition makes the compiler wait for it at the
+    // branch's end, one memory round trip per piece
     auto a_load_to = [&](int ch, u32x4_t (&v)[APT]) {
 #pragma unroll
         for (int j = 0; j < APT; ++j) {
             const int piece = tid + j * (64 * kDecWaves);
             const int row = piece >> 6, col = ch * kChunk + (piece & 63) * 8;
-            if (row < ntok && col < K) v[j] = *reinterpret_cast<const u32x4_t*>(arows[row] + col);
+            v[j] = *reinterpret_cast<const u32x4_t*>(arows[row < ntok ? row : 0] + (col < K ? col : K - 8));
         }
     };
     auto a_store_from = [&](int ch, const u32x4_t (&v)[APT], uint16_t* b) {
@@ -483,6 +488,453 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm2_kernel(GemmArgs a) {
         }
     };
     dec_stream<1, TGM, DEPTH, RGS, FULLA, SEG>(s_arow, ntok, F, codes, scales, cstride, sstride, lds, epi);
+}
+
+// ---------------------------------------------------------------------------
+// Small-batch layer in one persistent launch (T <= 16 tokens, d, F <= 4096).
+//
+// At a few tokens the layer's own work is small (T = 1 on the 160-expert shard
+// streams ~5 experts, 35 MB) and separate launches for routing, permutation,
+// the two GEMMs and the combine cost more than the work.  One workgroup per
+// CU runs every step, with three grid-wide barriers:
+//   1. router logits in fp64 (exact sums of the bf16 x bf16 products, in a
+//      fixed order; experts spread over the workgroups) and, in W4A4, the
+//      NVFP4 quantize-dequantize of the token rows;           -- barrier --
+//   2. every workgroup reads the logits and takes the same top-k selection
+//      (descending logit, equal logits: lower id), softmax over the k, shard
+//      filter and the pair order (local expert, token) into its own LDS, so no
+//      table crosses workgroups;
+//   3. GEMM1 + SwiGLU in units of 32 SwiGLU columns of one expert (the
+//      weight-streaming kernel's block-diagonal MFMA, the expert's tokens as up
+//      to four token groups);                                  -- barrier --
+//   4. GEMM2 in units of 256 output columns;                   -- barrier --
+//   5. the weighted combine (slot order, then the shared row), as combine_kernel.
+// The barriers need every workgroup resident at once: the launch has one
+// workgroup per CU and ~150 KB of LDS each, so no two share a CU, and the
+// preceding stream work has finished.  A barrier's wait is bounded: past
+// kMicroSpin polls the workgroup sets the error word and goes on (the output
+// is then wrong, but the kernel ends).  The counter and the error word are
+// zeroed by micro_reset_kernel, enqueued just before.
+// ---------------------------------------------------------------------------
+constexpr int kMicroMaxT = 16;
+constexpr int kMicroMaxDim = 4096;          // d and F: the 16-row whole-K token stage fits the LDS
+                                            // (also the T x d token rows of the logits phase)
+constexpr int kMicroMaxL = 1024;
+constexpr unsigned kMicroSpin = 1u << 22;   // polls (each after a ~60 ns sleep) before giving up
+
+__global__ void micro_reset_kernel(unsigned* bar) {
+    if (threadIdx.x < 2) bar[threadIdx.x] = 0u;
+}
+
+// Arrive at barrier number `n` (1, 2, 3) of the launch and wait for all `nwg`
+// workgroups: release this workgroup's writes device-wide, count, wait
+// (bounded), acquire the others'.  The wait polls with relaxed device-scope
+// loads (coherent, and no cache invalidation per poll: an acquire in the loop
+// would invalidate the caches on every poll while other workgroups still
+// stream); the acquire fence comes once, after the wait.
+__device__ __forceinline__ void micro_grid_barrier(unsigned* bar, unsigned n, unsigned nwg) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned target = n * nwg;
+        unsigned polls = 0;
+        while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++polls > kMicroSpin) {
+                __hip_atomic_fetch_or(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+template <bool SEG1, bool SEG2>
+__global__ __launch_bounds__(64 * kDecWaves) void micro_layer_kernel(MicroArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];   // dec_stream's token stage
+    __shared__ uint32_t s_mask[kMicroMaxL];          // per local expert: its tokens (bit t)
+    __shared__ int s_off[kMicroMaxL + 1];            // first pair row of each local expert
+    __shared__ int s_list[kMicroMaxL + 1];           // touched local experts, ascending
+    __shared__ int s_nlist;
+    __shared__ float s_w[kMicroMaxT * 32];           // routing weight of pair t k + j
+    __shared__ int s_inv[kMicroMaxT * 32];           // its row (-1: outside the shard)
+    __shared__ const uint16_t* s_arow[16];
+    __shared__ float s_up[2][2][4][64];
+    __shared__ double s_red[kDecWaves][kMicroMaxT];
+    __shared__ double s_top[kMicroMaxT][32];         // selected logits of each token, slot order
+    __shared__ int s_topid[kMicroMaxT][32];
+    __shared__ int s_wsum[kDecWaves];
+
+    const int T = a.T, d = a.d, F = a.F, E = a.E, k = a.topk, L = a.L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const unsigned wg = blockIdx.x, nwg = gridDim.x;
+    const uint16_t* act_in = a.mode == 0 ? a.X : a.hq;
+
+    // ---- 1. logits (fp64, fixed order) and the W4A4 token rows ----
+    // the T token rows go to LDS once (the token-stage region is free until the
+    // GEMMs); a thread then takes 8 consecutive k of an expert's gate row per
+    // 16-byte load, pieces tid, tid + 256, ... in order
+    if ((int)wg < E) {
+        const int pieces = T * (d / 8);
+        for (int q0 = 0; q0 < pieces; q0 += 8 * 64 * kDecWaves) {
+            u32x4_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = q0 + j * 64 * kDecWaves + tid;
+                v[j] = *reinterpret_cast<const u32x4_t*>(a.X + (size_t)(q < pieces ? q : pieces - 1) * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = q0 + j * 64 * kDecWaves + tid;
+                if (q < pieces) *reinterpret_cast<u32x4_t*>(lds + (size_t)q * 8) = v[j];
+            }
+        }
+        __syncthreads();
+    }
+    for (int e = (int)wg; e < E; e += (int)nwg) {
+        double acc[kMicroMaxT];
+#pragma unroll
+        for (int t = 0; t < kMicroMaxT; ++t) acc[t] = 0.0;
+        const uint16_t* g = a.G + (size_t)e * d;
+        for (int q = tid; q < d / 8; q += 64 * kDecWaves) {
+            const u32x4_t gv4 = *reinterpret_cast<const u32x4_t*>(g + q * 8);
+            const uint32_t gw[4] = {gv4.x, gv4.y, gv4.z, gv4.w};
+            double gv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gv[2 * i] = (double)bf16_bits_to_f32(gw[i] & 0xFFFFu);
+                gv[2 * i + 1] = (double)bf16_bits_to_f32(gw[i] >> 16);
+            }
+#pragma unroll
+            for (int t = 0; t < kMicroMaxT; ++t) {
+                if (t < T) {
+                    const u32x4_t xv4 = *reinterpret_cast<const u32x4_t*>(lds + (size_t)t * d + q * 8);
+                    const uint32_t xw[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[t] = fma((double)bf16_bits_to_f32(xw[i] & 0xFFFFu), gv[2 * i], acc[t]);
+                        acc[t] = fma((double)bf16_bits_to_f32(xw[i] >> 16), gv[2 * i + 1], acc[t]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kMicroMaxT; ++t) {
+            if (t < T) {
+                const double v = wave_sum_f64(acc[t]);
+                if (lane == 0) s_red[wave][t] = v;
+            }
+        }
+        __syncthreads();
+        if (tid < T) {
+            double v = s_red[0][tid];
+#pragma unroll
+            for (int w = 1; w < kDecWaves; ++w) v += s_red[w][tid];
+            a.logits[(size_t)tid * E + e] = v;
+        }
+        __syncthreads();
+    }
+    if (a.mode == 1) {
+        const int nb = T * (d / kBlock);
+        for (int b = (int)(wg * 64 * kDecWaves) + tid; b < nb; b += (int)(nwg * 64 * kDecWaves)) {
+            const uint16_t* x = a.X + (size_t)b * kBlock;
+            float f[16];
+            float bmax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                f[i] = bf16_bits_to_f32(x[i]);
+                bmax = fmaxf(bmax, fabsf(f[i]));
+            }
+            uint32_t o[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                o[i] = pack_hi16(nvfp4_fake_quant(f[2 * i], bmax, a.a1g), nvfp4_fake_quant(f[2 * i + 1], bmax, a.a1g));
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(a.hq + (size_t)b * kBlock);
+            dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+            dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+        }
+    }
+    micro_grid_barrier(a.bar, 1, nwg);
+
+    // ---- 2. selection, shard filter and pair order (every workgroup alike) ----
+    for (int l = tid; l < L; l += 64 * kDecWaves) s_mask[l] = 0u;
+    __syncthreads();
+    for (int t = wave; t < T; t += kDecWaves) {
+        constexpr int EPL = kMaxExpertsMicro / 64;
+        double v[EPL];
+#pragma unroll
+        for (int sl = 0; sl < EPL; ++sl) {
+            const int e = lane + 64 * sl;
+            v[sl] = a.logits[(size_t)t * E + (e < E ? e : E - 1)];   // unconditional (slots past E are never taken)
+        }
+        bool taken[EPL];
+#pragma unroll
+        for (int sl = 0; sl < EPL; ++sl) taken[sl] = lane + 64 * sl >= E;
+        for (int r = 0; r < k; ++r) {
+            double bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int sl = 0; sl < EPL; ++sl)
+                if (!taken[sl] && (v[sl] > bv || (v[sl] == bv && lane + 64 * sl < bi))) {
+                    bv = v[sl];
+                    bi = lane + 64 * sl;
+                }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const double ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+#pragma unroll
+            for (int sl = 0; sl < EPL; ++sl)
+                if (lane + 64 * sl == bi) taken[sl] = true;
+            if (lane == 0) {
+                s_top[t][r] = bv;
+                s_topid[t][r] = bi;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) {
+            double zs = 0.0;
+            for (int j = 0; j < k; ++j) zs += exp(s_top[t][j] - s_top[t][0]);
+            for (int j = 0; j < k; ++j) {
+                s_w[t * k + j] = (float)(exp(s_top[t][j] - s_top[t][0]) / zs);
+                const int lam = s_topid[t][j] - a.offset;
+                s_inv[t * k + j] = (lam >= 0 && lam < L) ? lam : -1;     // local id for now
+                if (lam >= 0 && lam < L) atomicOr(&s_mask[lam], 1u << t);
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive scans over the local experts of (pair count, touched), in order
+    {
+        constexpr int PER = kMicroMaxL / (64 * kDecWaves);
+        int c[PER], u[PER], cs = 0, us = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int l = tid * PER + i;
+            c[i] = l < L ? __popc(s_mask[l]) : 0;
+            u[i] = c[i] > 0;
+            cs += c[i];
+            us += u[i];
+        }
+        // wave-inclusive scans of (cs, us) packed in one int (counts < 2^15 each)
+        int pk = cs | (us << 16), inc = pk;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) s_wsum[wave] = inc;
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += s_wsum[w];
+        int ex = base + inc - pk;
+        int pc = ex & 0xFFFF, pu = ex >> 16;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int l = tid * PER + i;
+            if (l < L) {
+                s_off[l] = pc;
+                if (u[i]) s_list[pu] = l;
+            }
+            pc += c[i];
+            pu += u[i];
+        }
+        if (tid == 64 * kDecWaves - 1) {
+            s_off[L] = pc;
+            s_nlist = pu;
+        }
+    }
+    __syncthreads();
+    // pair rows for the combine: local pair (t, j) -> s_off[lam] + rank of t
+    for (int p = tid; p < T * k; p += 64 * kDecWaves) {
+        const int lam = s_inv[p];
+        if (lam >= 0) {
+            const int t = p / k;
+            s_inv[p] = s_off[lam] + __popc(s_mask[lam] & ((1u << t) - 1u));
+        }
+    }
+    __syncthreads();
+    const int nlist = s_nlist;
+    const int ngroups = nlist + (a.has_shared ? 1 : 0);
+    const int shared_row0 = T * k;
+
+    // the unit's token rows: group i < nlist is local expert s_list[i], else the shared expert
+    auto group_rows = [&](int i, const uint16_t* base, int stride, bool pair_rows) -> int {
+        int ntok;
+        if (i < nlist) {
+            const int lam = s_list[i];
+            const uint32_t m = s_mask[lam];
+            ntok = __popc(m);
+            if (tid < 16 && tid < ntok) {
+                // tid-th set bit of m
+                uint32_t mm = m;
+                for (int q = 0; q < tid; ++q) mm &= mm - 1u;
+                const int t = __ffs(mm) - 1;
+                s_arow[tid] = base + (size_t)(pair_rows ? s_off[lam] + tid : t) * stride;
+            }
+        } else {
+            ntok = T;
+            if (tid < T) s_arow[tid] = base + (size_t)(pair_rows ? shared_row0 + tid : tid) * stride;
+        }
+        __syncthreads();
+        return ntok;
+    };
+    auto group_weights = [&](int i, const ExpertWeights*& W, size_t& ex) {
+        const bool sh = i >= nlist;
+        W = sh ? &a.shared : &a.local;
+        ex = sh ? 0 : (size_t)s_list[i];
+    };
+
+    // ---- 3. GEMM1 + SwiGLU: unit = (group, 32 SwiGLU columns) ----
+    {
+        const int half = wave & 1;
+        const bool is_up = wave >= 2;
+        const int n = lane & 15, g = lane >> 4;
+        const int ncg = F / 32;
+        for (int u = (int)wg; u < ngroups * ncg; u += (int)nwg) {
+            const int i = u / ncg, cg = u - i * ncg;
+            const ExpertWeights* W;
+            size_t ex;
+            group_weights(i, W, ex);
+            const int ntok = group_rows(i, act_in, d, false);
+            const int row0 = i < nlist ? s_off[s_list[i]] : shared_row0;
+            const int col0 = cg * 32 + half * 16;
+            const uint8_t* w13 = W->w13 + ex * (size_t)(2 * F) * (d / 2);
+            const uint8_t* w13s = W->w13_s + ex * (size_t)(2 * F) * (d / 16);
+            const int wrow = (is_up ? F : 0) + col0 + n;
+            const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2)};
+            const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16)};
+            const float g13 = W->g13[ex] * a.a1g;
+            auto epi = [&](int j, const f32x4_t (&acc)[4][1]) {
+                const int col = col0 + n;
+                float v[4];
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) v[tg] = dec_result<4, 1>(acc, tg, 0, g) * g13;
+                if (is_up) {
+#pragma unroll
+                    for (int tg = 0; tg < 4; ++tg) s_up[j & 1][half][tg][lane] = v[tg];
+                }
+                __syncthreads();
+                if (!is_up) {
+#pragma unroll
+                    for (int tg = 0; tg < 4; ++tg) {
+                        const float gt = v[tg], up = s_up[j & 1][half][tg][lane];
+                        float av = gt / (1.0f + expf(-gt)) * up;
+                        if (a.mode == 1) {
+                            float m = fabsf(av);
+                            m = fmaxf(m, __shfl_xor(m, 1, 64));
+                            m = fmaxf(m, __shfl_xor(m, 2, 64));
+                            m = fmaxf(m, __shfl_xor(m, 4, 64));
+                            m = fmaxf(m, __shfl_xor(m, 8, 64));
+                            av = nvfp4_fake_quant(av, m, a.a2g);
+                        }
+                        const int r = tg * 4 + g;
+                        if (r < ntok) a.act[(size_t)(row0 + r) * F + col] = (uint16_t)f32_to_bf16_rne(av);
+                    }
+                }
+            };
+            dec_stream<1, 4, 4, 1, true, SEG1>(s_arow, ntok, d, codes, scales, (size_t)32 * (d / 2),
+                                              (size_t)32 * (d / 16), lds, epi);
+            __syncthreads();                         // s_arow, s_up and the token stage are free again
+        }
+    }
+    micro_grid_barrier(a.bar, 2, nwg);
+
+    // ---- 4. GEMM2: unit = (group, 256 output columns; four row groups per wave) ----
+    {
+        const int n = lane & 15, g = lane >> 4;
+        const int ncb = d / 256;
+        for (int u = (int)wg; u < ngroups * ncb; u += (int)nwg) {
+            const int i = u / ncb, cb = u - i * ncb;
+            const ExpertWeights* W;
+            size_t ex;
+            group_weights(i, W, ex);
+            const int ntok = group_rows(i, a.act, F, true);
+            const int row0 = i < nlist ? s_off[s_list[i]] : shared_row0;
+            const int cbase = cb * 256 + wave * 16;
+            const uint8_t* w2 = W->w2 + ex * (size_t)d * (F / 2);
+            const uint8_t* w2s = W->w2_s + ex * (size_t)d * (F / 16);
+            const uint8_t* const codes[1] = {w2 + (size_t)(cbase + n) * (F / 2)};
+            const uint8_t* const scales[1] = {w2s + (size_t)(cbase + n) * (F / 16)};
+            const float g2 = W->g2[ex] * a.a2g;
+            auto epi = [&](int j, const f32x4_t (&acc)[4][1]) {
+                const int col = cbase + j * 64 + n;
+#pragma unroll
+                for (int tg = 0; tg < 4; ++tg) {
+                    const float y = dec_result<4, 1>(acc, tg, 0, g);
+                    const int r = tg * 4 + g;
+                    if (r < ntok) a.Y[(size_t)(row0 + r) * d + col] = (uint16_t)f32_to_bf16_rne(y * g2);
+                }
+            };
+            dec_stream<1, 4, 4, 4, true, SEG2>(s_arow, ntok, F, codes, scales, (size_t)64 * (F / 2),
+                                              (size_t)64 * (F / 16), lds, epi);
+            __syncthreads();
+        }
+    }
+    micro_grid_barrier(a.bar, 3, nwg);
+
+    // ---- 5. combine: slot order, then the shared row ----
+    const int per_row = d / 8;
+    for (int idx = (int)(wg * 64 * kDecWaves) + tid; idx < T * per_row; idx += (int)(nwg * 64 * kDecWaves)) {
+        const int t = idx / per_row, c0 = (idx - t * per_row) * 8;
+        float sacc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; ++j) {
+            const int row = s_inv[t * k + j];
+            if (row < 0) continue;
+            const float wj = s_w[t * k + j];
+            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(a.Y + (size_t)row * d + c0);
+            const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sacc[2 * e] = fmaf(wj, bf16_bits_to_f32(yw[e] & 0xFFFFu), sacc[2 * e]);
+                sacc[2 * e + 1] = fmaf(wj, bf16_bits_to_f32(yw[e] >> 16), sacc[2 * e + 1]);
+            }
+        }
+        if (a.has_shared) {
+            const u32x4_t y = *reinterpret_cast<const u32x4_t*>(a.Y + (size_t)(shared_row0 + t) * d + c0);
+            const uint32_t yw[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sacc[2 * e] = fmaf(1.0f, bf16_bits_to_f32(yw[e] & 0xFFFFu), sacc[2 * e]);
+                sacc[2 * e + 1] = fmaf(1.0f, bf16_bits_to_f32(yw[e] >> 16), sacc[2 * e + 1]);
+            }
+        }
+        u32x4_t o;
+        o.x = f32_to_bf16_rne(sacc[0]) | (f32_to_bf16_rne(sacc[1]) << 16);
+        o.y = f32_to_bf16_rne(sacc[2]) | (f32_to_bf16_rne(sacc[3]) << 16);
+        o.z = f32_to_bf16_rne(sacc[4]) | (f32_to_bf16_rne(sacc[5]) << 16);
+        o.w = f32_to_bf16_rne(sacc[6]) | (f32_to_bf16_rne(sacc[7]) << 16);
+        *reinterpret_cast<u32x4_t*>(a.out + (size_t)t * d + c0) = o;
+    }
+}
+
+bool micro_ok(int T, int d, int F, int E, int topk, int L) {
+    return T >= 1 && T <= kMicroMaxT && d <= kMicroMaxDim && F <= kMicroMaxDim && d % 256 == 0 && F % 32 == 0 &&
+           E <= kMaxExpertsMicro && topk <= 32 && L <= kMicroMaxL;
+}
+
+int micro_lds_bytes(int d, int F) { return dec_lds_bytes(16, d > F ? d : F, true); }
+
+hipError_t launch_micro(const MicroArgs& a, int ncu, hipStream_t s) {
+    hipLaunchKernelGGL(micro_reset_kernel, dim3(1), dim3(64), 0, s, a.bar);
+    const int lds = micro_lds_bytes(a.d, a.F);
+    const bool seg1 = a.d % 1024 == 0, seg2 = a.F % 1024 == 0;
+    auto go = [&](auto kern) {
+        if (allow_dynamic_lds<decltype(kern)::value>(lds) != hipSuccess) return;
+        hipLaunchKernelGGL(decltype(kern)::value, dim3(ncu), dim3(64 * kDecWaves), lds, s, a);
+    };
+    if (seg1 && seg2) go(std::integral_constant<decltype(&micro_layer_kernel<true, true>), &micro_layer_kernel<true, true>>{});
+    else if (seg1) go(std::integral_constant<decltype(&micro_layer_kernel<true, false>), &micro_layer_kernel<true, false>>{});
+    else if (seg2) go(std::integral_constant<decltype(&micro_layer_kernel<false, true>), &micro_layer_kernel<false, true>>{});
+    else go(std::integral_constant<decltype(&micro_layer_kernel<false, false>), &micro_layer_kernel<false, false>>{});
+    return hipGetLastError();
 }
 
 // Tile height of the decode path: 4 token rows (one group) while experts expect

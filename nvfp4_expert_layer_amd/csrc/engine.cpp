@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -78,7 +79,7 @@ struct Plan {
     int KS = 1, path = 1, BM = 16, max_tiles = 0, nblk = 0;
     bool exact = false;  // routing by exact fp64 logits (few tokens), else certified
     size_t rows = 0;  // rows of the expanded (pair + shared) activation space
-    size_t part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
+    size_t bar, part, xn2, gn2, topk_ids, topk_w, local_ids, rank, block_counts, counts, offsets, tiles,
         ntiles, perm, inv, hq, act, Y, total;
 };
 
@@ -89,7 +90,7 @@ int check_problem(const moe_nvfp4_problem* p) {
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown mode %d", p->mode);
     if (p->mode == MOE_NVFP4_W4A4_STATIC && (!global_ok(p->act_global13) || !global_ok(p->act_global2)))
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "static W4A4 activation globals must be finite, in 2^-100..2^100");
-    if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_MID)
+    if (p->path < MOE_NVFP4_PATH_AUTO || p->path > MOE_NVFP4_PATH_MICRO)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "unknown path %d", p->path);
     if (p->has_shared != 0 && p->has_shared != 1)
         return fail(MOE_NVFP4_ERR_INVALID_ARG, "has_shared must be 0 or 1");
@@ -108,6 +109,10 @@ int check_problem(const moe_nvfp4_problem* p) {
         return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "d_ff %d: need a multiple of 128 in 128..16384", p->d_ff);
     if (p->path == MOE_NVFP4_PATH_MID && !moe::mid_ok(p->d_model, p->d_ff))
         return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "the dense weight-streaming path needs d_model %% 256 == 0");
+    if (p->path == MOE_NVFP4_PATH_MICRO && p->num_tokens > 0 &&
+        !moe::micro_ok(p->num_tokens, p->d_model, p->d_ff, p->num_experts, p->top_k, p->num_local_experts))
+        return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE,
+                    "the one-launch small-batch path needs 1..16 tokens, d_model and d_ff <= 4096, d_model %% 256 == 0");
     // index arithmetic: pair rows and per-row offsets stay within int32
     const long long rows = (long long)p->num_tokens * (p->top_k + 1);
     if (rows > (1LL << 27)) return fail(MOE_NVFP4_ERR_UNSUPPORTED_SHAPE, "num_tokens * (top_k + 1) > 2^27");
@@ -127,7 +132,8 @@ void make_plan(const moe_nvfp4_problem& p, Plan& pl) {
     pl.rows = T * k + (p.has_shared ? T : 0);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes); return r; };
-    pl.part = take((size_t)pl.KS * T * E * (pl.exact ? 8 : 4));
+    pl.bar = take(2 * sizeof(unsigned));              // the one-launch path's grid barrier and error word
+    pl.part = take(std::max((size_t)pl.KS * T * E * (pl.exact ? 8 : 4), T * E * 8));
     pl.xn2 = take(pl.exact ? 0 : (size_t)pl.KS * T * 8);
     pl.gn2 = take(pl.exact ? 0 : (size_t)pl.KS * E * 8);
     pl.topk_ids = take(T * k * 4);
@@ -166,6 +172,21 @@ int current_arch_ok(int* dev_out) {
         cache[dev] = arch_ok(prop.gcnArchName) ? 1 : 2;
     }
     if (cache[dev] != 1) return fail(MOE_NVFP4_ERR_ARCH, "device %d is not gfx950", dev);
+    return MOE_NVFP4_OK;
+}
+
+// Compute units of the current device `dev` (cached per device).
+int cu_count(int dev, int* out) {
+    static std::mutex mu;
+    static int cache[64];
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return fail(MOE_NVFP4_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+        cache[dev] = n;
+    }
+    *out = cache[dev];
     return MOE_NVFP4_OK;
 }
 
@@ -337,6 +358,32 @@ int moe_nvfp4_forward_timed(const moe_nvfp4_problem* p, const void* hidden, cons
         return MOE_NVFP4_OK;
     };
     if ((st = mark(0))) return st;
+    if (pl.path == MOE_NVFP4_PATH_MICRO) {
+        // the whole layer in one persistent launch (after the barrier reset)
+        int ncu;
+        if ((st = cu_count(dev, &ncu))) return st;
+        const bool stat = p->mode == MOE_NVFP4_W4A4_STATIC;
+        moe::MicroArgs m{};
+        m.T = p->num_tokens; m.d = p->d_model; m.F = p->d_ff; m.E = p->num_experts; m.topk = p->top_k;
+        m.offset = p->local_expert_offset; m.L = p->num_local_experts; m.has_shared = p->has_shared;
+        m.mode = is_w4a4(p->mode) ? 1 : 0;
+        m.a1g = stat ? p->act_global13 : 1.0f;
+        m.a2g = stat ? p->act_global2 : 1.0f;
+        m.X = static_cast<const uint16_t*>(hidden);
+        m.G = static_cast<const uint16_t*>(gate_w);
+        m.local = to_internal(local);
+        m.shared = to_internal(p->has_shared ? shared : nullptr);
+        m.bar = at<unsigned>(workspace, pl.bar);
+        m.logits = at<double>(workspace, pl.part);
+        m.hq = at<uint16_t>(workspace, pl.hq);
+        m.act = at<uint16_t>(workspace, pl.act);
+        m.Y = at<uint16_t>(workspace, pl.Y);
+        m.out = static_cast<uint16_t*>(out);
+        if ((st = hip_status(moe::launch_micro(m, ncu, s), "small-batch layer launch"))) return st;
+        for (int i = 1; i < 6; ++i)
+            if ((st = mark(i))) return st;
+        return ok();
+    }
     if ((st = run_route(*p, pl, hidden, gate_w, workspace, s, nullptr, nullptr, nullptr, nullptr, nullptr)))
         return st;
     if ((st = mark(1))) return st;

@@ -68,6 +68,22 @@ struct GemmArgs {
     uint8_t* act_scales;          // [R][F/16]
 };
 
+// The small-batch layer in one launch (T <= 16): workspace regions and the problem.
+struct MicroArgs {
+    int T, d, F, E, topk, offset, L, has_shared, mode;
+    float a1g, a2g;
+    const uint16_t* X;            // bf16 [T][d]
+    const uint16_t* G;            // bf16 [E][d]
+    ExpertWeights local, shared;
+    unsigned* bar;                // [2]: grid barrier counter, error word (zeroed per launch)
+    double* logits;               // [T][E]
+    uint16_t* hq;                 // W4A4: [T][d] bf16 quantize-dequantized token rows
+    uint16_t* act;                // [T*k + T][F] bf16
+    uint16_t* Y;                  // [T*k + T][d] bf16
+    uint16_t* out;                // [T][d]
+};
+constexpr int kMaxExpertsMicro = 1024;
+
 struct CombineArgs {
     int T, d, topk, has_shared;
     const float* topk_w;          // [T][k]
@@ -101,6 +117,9 @@ hipError_t launch_gemm2(const GemmArgs& a, int path, hipStream_t s);
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s);
 hipError_t launch_dec_gemm2(const GemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+bool micro_ok(int T, int d, int F, int E, int topk, int L);   // the one-launch small-batch layer applies
+int micro_lds_bytes(int d, int F);
+hipError_t launch_micro(const MicroArgs& a, int ncu, hipStream_t s);
 bool mid_ok(int d, int F);                        // dense weight-streaming kernels apply
 bool mid_packed_ok(int d, int F);                 // ... with W4A4 activations as NVFP4
 int mid_rows();                                   // rows per tile of the dense weight-streaming path

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
         for (int j = 0; j < APT; ++j) {
             const int piece = tid + j * (64 * kMidWaves);
             const int row = piece >> 5, col = st * kMidKS + (piece & 31) * 8;
-            if (col < K) va[j] = *reinterpret_cast<const u32x4_t*>(s_arow[row] + col);
+            va[j] = *reinterpret_cast<const u32x4_t*>(s_arow[row] + (col < K ? col : K - 8));   // unconditional
         }
     };
     auto a_store = [&](int st, uint16_t* b) {
@@ -376,16 +376,16 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
         const int total = ROWS * (cp + sp);
         for (int p0 = 0; p0 < total; p0 += 8 * 64 * kMidWaves) {
             u32x4_t v[8];
+            // loads unconditional (clamped; see dec_stream), stores conditional
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int p = p0 + j * 64 * kMidWaves + tid;
-                if (p < ROWS * cp) {
-                    const int row = p / cp, c = p - row * cp;
-                    v[j] = *reinterpret_cast<const u32x4_t*>(acodes + (size_t)s_arow[row] * (K / 2) + c * 16);
-                } else if (p < total) {
-                    const int q = p - ROWS * cp, row = q / sp, c = q - row * sp;
-                    v[j] = *reinterpret_cast<const u32x4_t*>(ascales + (size_t)s_arow[row] * (K / 16) + c * 16);
-                }
+                const int p = min(p0 + j * 64 * kMidWaves + tid, total - 1);
+                const bool code = p < ROWS * cp;
+                const int q = code ? p : p - ROWS * cp;
+                const int per = code ? cp : sp;
+                const int row = q / per, c = q - row * per;
+                const uint8_t* src = code ? acodes + (size_t)s_arow[row] * (K / 2) : ascales + (size_t)s_arow[row] * (K / 16);
+                v[j] = *reinterpret_cast<const u32x4_t*>(src + c * 16);
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {

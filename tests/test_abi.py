@@ -138,5 +138,17 @@ def test_mid_path_needs_d_multiple_of_256():
     p = nv.make_problem(64, 512, 256, 16, 2, 0, 16, True, nv.W4A16, nv.PATH_MID)
     assert nv.moe_nvfp4_validate(p, 1 << 30, None) == nv.OK
     assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_MID
-    bad = nv.make_problem(64, 512, 256, 16, 2, 0, 16, True, nv.W4A16, 4)
+    bad = nv.make_problem(64, 512, 256, 16, 2, 0, 16, True, nv.W4A16, 5)
     assert nv.moe_nvfp4_validate(bad, 1 << 30, None) == nv.ERR_INVALID_ARG
+
+
+def test_micro_path_limits():
+    def st(T, d=4096, F=1024, E=320, k=8, L=160):
+        return nv.moe_nvfp4_validate(nv.make_problem(T, d, F, E, k, 0, L, True, nv.W4A16, nv.PATH_MICRO), 1 << 30)
+    assert st(1) == nv.OK and st(16) == nv.OK
+    assert st(0) == nv.OK                                   # an empty batch enqueues nothing
+    assert st(17) == nv.ERR_UNSUPPORTED_SHAPE
+    assert st(8, d=8192) == nv.ERR_UNSUPPORTED_SHAPE
+    assert st(8, F=8192) == nv.ERR_UNSUPPORTED_SHAPE
+    assert st(8, d=384) == nv.ERR_UNSUPPORTED_SHAPE          # d % 256
+    assert st(8, E=1024, k=32, L=1024) == nv.OK
