@@ -110,11 +110,14 @@ typedef enum {
 
 /* Kernel path.  AUTO picks from the expected number of local pairs per local
  * expert, T * top_k / num_experts (the shard's expected load, not the global
- * one): weight-streaming kernels up to 9 (W4A16, and W4A4 when d or F is not a
- * multiple of 256) or up to 6 (W4A4 with d and F multiples of 256, whose tiled
- * kernels move the activations as NVFP4), tiled kernels above.  Both paths give
- * results within the stated tolerances; they are not bit-identical to each
- * other. */
+ * one), with crossovers measured on the 4096 x 1024 layer:
+ *   W4A16 with d_model % 256 == 0: block-diagonal weight streaming (DECODE) up
+ *     to 5.5, dense weight streaming (MID) up to 22, tiles (PREFILL) above;
+ *   W4A4 with d_model and d_ff multiples of 256 (tiled kernels then move the
+ *     activations as NVFP4): DECODE up to 6, PREFILL above;
+ *   any other shape: DECODE up to 9, PREFILL above.
+ * AUTO never takes MICRO.  Every path gives results within the stated
+ * tolerances; they are not bit-identical to each other. */
 typedef enum {
     MOE_NVFP4_PATH_AUTO = 0,
     MOE_NVFP4_PATH_DECODE = 1,   /* weight streaming, block-diagonal MFMA, 4-16-row tiles */
@@ -166,8 +169,8 @@ int moe_nvfp4_workspace_size(const moe_nvfp4_problem *p, size_t *bytes);
  * (given non-null tensor pointers). */
 int moe_nvfp4_validate(const moe_nvfp4_problem *p, size_t workspace_bytes, const char *arch);
 
-/* The kernel path moe_nvfp4_forward takes for `p` (PATH_DECODE or
- * PATH_PREFILL: AUTO resolved by the rule above).  Device-free.  Writes it to
+/* The kernel path moe_nvfp4_forward takes for `p` (p->path itself unless it
+ * is AUTO, else the rule above resolves it).  Device-free.  Writes it to
  * *path and returns OK, or INVALID_ARG / UNSUPPORTED_SHAPE for a bad problem. */
 int moe_nvfp4_resolved_path(const moe_nvfp4_problem *p, int32_t *path);
 
