@@ -17,6 +17,9 @@
 //     1.0 the code value), used with a packed f16 multiply by the block scale on
 //     the W4A4 tiled path (exact: products of at most 6 significant bits in
 //     f16's normal range); covered by that path's parity tests.
+//   v_cvt_scalef32_pk_f16_fp8: two E4M3fn bytes (the low or high 16 bits of
+//     the source) -> two f16; with scale 1.0 exact for every finite E4M3 value
+//     (its subnormals, down to 2^-9, are f16 normals).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,6 +55,16 @@ __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
     return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Two E4M3 block scales (bytes 0 and 1 of `pair`) -> f16 {byte 0, byte 1}.
+__device__ __forceinline__ f16x2_t e4m3x2_to_f16(uint32_t pair) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pair, 1.0f, false);
+}
+
+// Bytes 2 and 3 of `quad` -> f16 {byte 2, byte 3}.
+__device__ __forceinline__ f16x2_t e4m3x2_hi_to_f16(uint32_t quad) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(quad, 1.0f, true);
 }
 
 // Two E2M1 codes (byte `sel` of `src`) -> exact fp32 values.

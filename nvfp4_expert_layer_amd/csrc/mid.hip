@@ -59,14 +59,6 @@ constexpr int kMidLdw = kMidKS + kMidPad;
 constexpr int kBufferFlags = 0x00020000;
 
 
-// Eight E2M1 codes (one dword, element 8j+e in nibble e) times a block scale
-// -> 8 exact 16-bit values (4 dwords) in the MFMA's operand type.
-template <int MODE>
-__device__ __forceinline__ u32x4_t mid_decode8(uint32_t codes, float s, f16x2_t s2) {
-    if constexpr (MODE == 1) return dequant8_f16(codes, s2);
-    else return dequant8_bf16(codes, s);
-}
-
 template <int MODE>
 __device__ __forceinline__ f32x4_t mid_mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
     if constexpr (MODE == 1)
@@ -206,9 +198,14 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const uint32_t cw = q < 4 ? rl[u][r][q] : rh[u][r][q - 4];
-                const float sf = e4m3_to_f32((rs[u][r] >> (8 * (q >> 1))) & 0xFFu);
-                const _Float16 sh = (_Float16)sf;
-                const u32x4_t bf = mid_decode8<MODE>(cw, sf, f16x2_t{sh, sh});
+                u32x4_t bf;
+                if constexpr (MODE == 1) {
+                    const f16x2_t sp = q < 4 ? e4m3x2_to_f16(rs[u][r]) : e4m3x2_hi_to_f16(rs[u][r]);
+                    const _Float16 sh = (q & 2) ? sp.y : sp.x;
+                    bf = dequant8_f16(cw, f16x2_t{sh, sh});
+                } else {
+                    bf = dequant8_bf16(cw, e4m3_to_f32((rs[u][r] >> (8 * (q >> 1))) & 0xFFu));
+                }
 #pragma unroll
                 for (int t = 0; t < TG; ++t) acc[r][t] = mid_mfma<MODE>(af[t], bf, acc[r][t]);
             }
@@ -482,13 +479,15 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
             u32x4_t af[TG];
 #pragma unroll
             for (int t = 0; t < TG; ++t) {
-                const _Float16 sa = (_Float16)e4m3_to_f32((asc[t] >> (8 * (q >> 1))) & 0xFFu);
+                const f16x2_t sp = q < 4 ? e4m3x2_to_f16(asc[t]) : e4m3x2_hi_to_f16(asc[t]);
+                const _Float16 sa = (q & 2) ? sp.y : sp.x;
                 af[t] = kvalid ? dequant8_f16(q < 4 ? alo[t][q] : ahi[t][q - 4], f16x2_t{sa, sa}) : zero4;
             }
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 const uint32_t cw = q < 4 ? rl[u][r][q] : rh[u][r][q - 4];
-                const _Float16 sb = (_Float16)e4m3_to_f32((rs[u][r] >> (8 * (q >> 1))) & 0xFFu);
+                const f16x2_t sp = q < 4 ? e4m3x2_to_f16(rs[u][r]) : e4m3x2_hi_to_f16(rs[u][r]);
+                const _Float16 sb = (q & 2) ? sp.y : sp.x;
                 const u32x4_t bf = dequant8_f16(cw, f16x2_t{sb, sb});
 #pragma unroll
                 for (int t = 0; t < TG; ++t) acc[r][t] = mid_mfma<1>(af[t], bf, acc[r][t]);

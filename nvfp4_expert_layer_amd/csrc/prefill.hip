@@ -241,12 +241,12 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
                 u32x4_t bv[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const uint32_t sbyte = (sc[j] >> (8 * (kk >> 1))) & 0xFFu;
                     if constexpr (MODE == 1) {
-                        const _Float16 s = (_Float16)e4m3_to_f32(sbyte);
+                        const f16x2_t sp = e4m3x2_to_f16(sc[j]);
+                        const _Float16 s = kk < 2 ? sp.x : sp.y;
                         bv[j] = dequant8_f16(rc[j][kk], f16x2_t{s, s});
                     } else {
-                        bv[j] = dequant8_bf16(rc[j][kk], e4m3_to_f32(sbyte));
+                        bv[j] = dequant8_bf16(rc[j][kk], e4m3_to_f32((sc[j] >> (8 * (kk >> 1))) & 0xFFu));
                     }
                 }
 #pragma unroll
@@ -508,17 +508,23 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
             bc[j] = *reinterpret_cast<const u32x4_t*>(S + kQCodes + swz(brow[j], 2 * s + h));
             bs[j] = *reinterpret_cast<const uint32_t*>(S + 2 * kQCodes + kQScales + brow[j] * 16 + s * 4) >> (16 * h);
         }
+        // the lane half's two block scales of the step, as f16 {MFMAs 0-1, 2-3}
+        f16x2_t asc[4], bsc[NJ];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) asc[i] = e4m3x2_to_f16(as[i]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bsc[j] = e4m3x2_to_f16(bs[j]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             u32x4_t av[4], bv[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const _Float16 sc = (_Float16)e4m3_to_f32((bs[j] >> (8 * (kk >> 1))) & 0xFFu);
+                const _Float16 sc = kk < 2 ? bsc[j].x : bsc[j].y;
                 bv[j] = dequant8_f16(bc[j][kk], f16x2_t{sc, sc});
             }
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                const _Float16 sc = (_Float16)e4m3_to_f32((as[i] >> (8 * (kk >> 1))) & 0xFFu);
+                const _Float16 sc = kk < 2 ? asc[i].x : asc[i].y;
                 av[i] = dequant8_f16(ac[i][kk], f16x2_t{sc, sc});
             }
 #pragma unroll
