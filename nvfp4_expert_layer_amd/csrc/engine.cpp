@@ -55,23 +55,27 @@ int resolve_path(const moe_nvfp4_problem& p) {
     if (p.path != MOE_NVFP4_PATH_AUTO) return p.path;
     // expected local pairs per local expert: T * k / E (uniform routing).  The
     // crossovers were measured on the 4096 x 1024 layer with 160 local experts
-    // (per-call medians):
-    //   W4A16: weight streaming with the block-diagonal kernels up to ~5.5 pairs
-    //   per expert (T = 192: 345 us against 355 dense), the dense
-    //   weight-streaming kernels up to ~22 (T = 384: 384 us against 539
-    //   block-diagonal and 552 tiled; T = 768: 575 against 627 tiled), then the
-    //   tiles (T = 1024: 621 against 650);
-    //   packed W4A4 (tiles moving NVFP4 activations, 3.5x fewer bytes): weight
-    //   streaming up to 6, tiles above (the dense kernels measured a few per
-    //   cent slower there: T = 512: 388 against 371 us);
-    //   W4A4 whose d or F rules out packed tiles: weight streaming up to 9.
+    // (per-call medians, us):
+    //   W4A16: block-diagonal weight streaming up to ~4.6 pairs per expert
+    //   (T = 176: 328 against 337 dense; T = 192: 346 against 340), the dense
+    //   weight-streaming kernels up to ~44 (T = 1536: 671 against 709 tiled;
+    //   T = 2048: 774 against 754), then the tiles;
+    //   W4A4 with the activations as NVFP4: block-diagonal up to 5 (T = 192:
+    //   311 against 313 dense; T = 224: 357 against 315), dense up to 18
+    //   (T = 704: 368 against 388 tiled; T = 768: 403 against 391), tiles above;
+    //   other shapes (no dense path, or W4A4 with 16-bit activations):
+    //   block-diagonal up to 6 (packed tiles) or 9, tiles above.
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
     const bool w4a4 = is_w4a4(p.mode);
-    const bool packed = w4a4 && moe::pf_packed_ok(p.d_model, p.d_ff);
     if (!w4a4 && moe::mid_ok(p.d_model, p.d_ff)) {
-        if (per_expert <= 5.5) return MOE_NVFP4_PATH_DECODE;
-        return per_expert <= 22.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
+        if (per_expert <= 4.6) return MOE_NVFP4_PATH_DECODE;
+        return per_expert <= 44.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
     }
+    if (w4a4 && moe::mid_packed_ok(p.d_model, p.d_ff)) {
+        if (per_expert <= 5.0) return MOE_NVFP4_PATH_DECODE;
+        return per_expert <= 18.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
+    }
+    const bool packed = w4a4 && moe::pf_packed_ok(p.d_model, p.d_ff);
     return per_expert <= (packed ? 6.0 : 9.0) ? MOE_NVFP4_PATH_DECODE : MOE_NVFP4_PATH_PREFILL;
 }
 

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 // ---------------------------------------------------------------------------
 int gemm_bm(int path, int T, int topk, int E, bool packed_mid) {
-    return path == 1 ? dec_rows(T, topk, E) : (path == 3 ? (packed_mid ? mid_rows_packed() : mid_rows()) : pf_rows());
+    return path == 1 ? dec_rows(T, topk, E) : (path == 3 ? (packed_mid ? mid_rows_packed() : mid_rows(T, topk, E)) : pf_rows());
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {

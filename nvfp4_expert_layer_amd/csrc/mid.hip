@@ -48,8 +48,8 @@
 
 namespace moe {
 
-constexpr int kMidWaves = 4;
-constexpr int kMidNR = 4;            // row groups of 16 weight rows per wave
+constexpr int kMidWaves = 8;
+constexpr int kMidNR = 2;            // row groups of 16 weight rows per wave
 constexpr int kMidDepth = 2;         // weight prefetch ring depth (steps of 256 k)
 constexpr int kMidKS = 256;          // K elements per step (and per LDS stage)
 constexpr int kMidPad = 8;           // 16-bit elements of padding per LDS row
@@ -75,7 +75,7 @@ __device__ __forceinline__ f32x4_t mid_mfma(const u32x4_t& a, const u32x4_t& b, 
 // grid is (max_tiles x column blocks), column blocks varying fastest so that
 // the workgroups of tiles past the table's end (which only return) come last.
 template <int KIND, int MODE, int TG>
-__global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(2))) void mid_gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(4))) void mid_gemm_kernel(GemmArgs a) {
     constexpr int ROWS = 16 * TG;
     constexpr int NR = kMidNR, DEPTH = kMidDepth;
     constexpr int APT = ROWS * (kMidKS / 8) / (64 * kMidWaves);   // 16-byte A pieces per thread per step
@@ -125,11 +125,11 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
             KIND == 1 ? W.w13_s + ex * (size_t)rows * (d / 16) : W.w2_s + ex * (size_t)rows * (F / 16);
         crs = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, rows * (K / 2), kBufferFlags);
         srs = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, rows * (K / 16), kBufferFlags);
-        const int wrow = KIND == 1 ? cb * 128 + wave * 32 + n : cb * 256 + wave * 64 + n;
+        const int wrow = KIND == 1 ? cb * 128 + wave * (8 * NR) + n : cb * 256 + wave * (16 * NR) + n;
         lane_c = wrow * (K / 2);
         lane_s = wrow * (K / 16);
     }
-    auto roff = [&](int r) -> int { return KIND == 1 ? (r >= 2 ? F : 0) + (r & 1) * 16 : r * 16; };
+    auto roff = [&](int r) -> int { return KIND == 1 ? (r >= NR / 2 ? F : 0) + (r % (NR / 2)) * 16 : r * 16; };
     const float gsc = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;   // weight x activation globals
 
     const int nsteps = (K + 255) / 256;                 // K % 128 == 0
@@ -230,13 +230,13 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
     // ---- epilogue: lane holds rows 4 g + i (+16 t) of columns n of each row group ----
     if (KIND == 1) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = cb * 128 + wave * 32 + h * 16 + n;
+        for (int h = 0; h < NR / 2; ++h) {
+            const int col = cb * 128 + wave * (8 * NR) + h * 16 + n;
 #pragma unroll
             for (int t = 0; t < TG; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float gt = acc[h][t][i] * gsc, up = acc[h + 2][t][i] * gsc;
+                    const float gt = acc[h][t][i] * gsc, up = acc[h + NR / 2][t][i] * gsc;
                     float av = gt / (1.0f + expf(-gt)) * up;
                     if (MODE == 1) {
                         // NVFP4 quantize-dequantize over the 16 columns held by lanes n = 0..15
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
     } else {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const int col = cb * 256 + wave * 64 + r * 16 + n;
+            const int col = cb * 256 + wave * (16 * NR) + r * 16 + n;
 #pragma unroll
             for (int t = 0; t < TG; ++t)
 #pragma unroll
@@ -282,7 +282,9 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
 // as in mid_gemm_kernel.  GEMM1's epilogue quantizes the SwiGLU output per 16
 // columns and writes it packed.
 // ---------------------------------------------------------------------------
-constexpr int kMid4Depth = 4;
+constexpr int kMid4Depth = 2;
+constexpr int kMid4Waves = 8;
+constexpr int kMid4NR = 2;           // row groups of 16 weight rows per wave
 constexpr int kMid4TG = 2;           // token groups: 32-row tiles
 constexpr int kMid4CodePad = 16;     // bytes of padding per LDS code row
 constexpr int kMid4ScalePad = 16;    // bytes of padding per LDS scale row (16 lanes read 16 rows' dwords)
@@ -293,8 +295,8 @@ __host__ __device__ constexpr int mid4_lds_bytes(int K) {
 }
 
 template <int KIND, int CBW>
-__global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(2))) void mid4_gemm_kernel(GemmArgs a) {
-    constexpr int NR = kMidNR, DEPTH = kMid4Depth, TG = kMid4TG, ROWS = 16 * TG;
+__global__ __launch_bounds__(64 * kMid4Waves) __attribute__((amdgpu_waves_per_eu(4))) void mid4_gemm_kernel(GemmArgs a) {
+    constexpr int NR = kMid4NR, DEPTH = kMid4Depth, TG = kMid4TG, ROWS = 16 * TG;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int s_arow[ROWS];
 
@@ -333,12 +335,12 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
             KIND == 1 ? W.w13_s + ex * (size_t)rows * (d / 16) : W.w2_s + ex * (size_t)rows * (F / 16);
         crs = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, rows * (K / 2), kBufferFlags);
         srs = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, rows * (K / 16), kBufferFlags);
-        const int wrow = KIND == 1 ? cbw * CBW * 128 + wave * 32 + n : cbw * CBW * 256 + wave * 64 + n;
+        const int wrow = KIND == 1 ? cbw * CBW * 128 + wave * (8 * NR) + n : cbw * CBW * 256 + wave * (16 * NR) + n;
         lane_c = wrow * (K / 2);
         lane_s = wrow * (K / 16);
     }
     auto roff = [&](int r, int j) -> int {
-        return KIND == 1 ? (r >= 2 ? F : 0) + (r & 1) * 16 + j * 128 : r * 16 + j * 256;
+        return KIND == 1 ? (r >= NR / 2 ? F : 0) + (r % (NR / 2)) * 16 + j * 128 : r * 16 + j * 256;
     };
     const float gsc = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;
 
@@ -371,12 +373,12 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
         const int cp = K / 32;                           // 16-byte code pieces per row
         const int sp = K / 256;                          // 16-byte scale pieces per row
         const int total = ROWS * (cp + sp);
-        for (int p0 = 0; p0 < total; p0 += 8 * 64 * kMidWaves) {
+        for (int p0 = 0; p0 < total; p0 += 8 * 64 * kMid4Waves) {
             u32x4_t v[8];
             // loads unconditional (clamped; see dec_stream), stores conditional
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int p = min(p0 + j * 64 * kMidWaves + tid, total - 1);
+                const int p = min(p0 + j * 64 * kMid4Waves + tid, total - 1);
                 const bool code = p < ROWS * cp;
                 const int q = code ? p : p - ROWS * cp;
                 const int per = code ? cp : sp;
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int p = p0 + j * 64 * kMidWaves + tid;
+                const int p = p0 + j * 64 * kMid4Waves + tid;
                 if (p < ROWS * cp) {
                     const int row = p / cp, c = p - row * cp;
                     *reinterpret_cast<u32x4_t*>(lcodes + row * CR + c * 16) = v[j];
@@ -410,13 +412,13 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
     auto epilogue = [&](int j) {
         if (KIND == 1) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int col0 = (cbw * CBW + j) * 128 + wave * 32 + h * 16;   // the block's first column
+            for (int h = 0; h < NR / 2; ++h) {
+                const int col0 = (cbw * CBW + j) * 128 + wave * (8 * NR) + h * 16;   // the block's first column
 #pragma unroll
                 for (int t = 0; t < TG; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float gt = acc[h][t][i] * gsc, up = acc[h + 2][t][i] * gsc;
+                        const float gt = acc[h][t][i] * gsc, up = acc[h + NR / 2][t][i] * gsc;
                         const float av = gt / (1.0f + expf(-gt)) * up;
                         // NVFP4 over the block's 16 columns (lanes n = 0..15 of lane group g)
                         float m = fabsf(av);
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
         } else {
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                const int col = (cbw * CBW + j) * 256 + wave * 64 + r * 16 + n;
+                const int col = (cbw * CBW + j) * 256 + wave * (16 * NR) + r * 16 + n;
 #pragma unroll
                 for (int t = 0; t < TG; ++t)
 #pragma unroll
@@ -517,13 +519,15 @@ __global__ __launch_bounds__(64 * kMidWaves) __attribute__((amdgpu_waves_per_eu(
 // F a multiple of 128 (always).
 bool mid_ok(int d, int F) { return d % 256 == 0 && F % 128 == 0; }
 
-// Token rows per tile: 16 (one MFMA token group).  Two token groups (32 rows,
-// one weight stream for up to 32 pairs) need more registers than two waves per
-// SIMD allow with the step's A staging; an expert with more than 16 pairs
-// streams its weights once per tile, the later tiles' workgroups right after
-// the first's on the same XCD (column blocks vary fastest).
-constexpr int kMidTG = 1;
-int mid_rows() { return 16 * kMidTG; }
+// Token rows per tile, from the expected pairs per local expert T k / E: 16
+// (one MFMA token group) up to 12, else 32 (one weight stream for up to 32
+// pairs, at twice the MFMA work per weight element).  An expert with more pairs
+// than a tile holds streams its weights once per tile, the later tiles'
+// workgroups right after the first's (column blocks vary fastest).  Measured on
+// the 4096 x 1024 layer with 160 local experts, W4A16, per layer: T = 384 (9.6
+// pairs per expert) 372 us with 16 rows against 396 with 32; T = 512 (12.8)
+// 413 against 408; T = 768 567 against 441.
+int mid_rows(int T, int topk, int E) { return (double)T * topk / E <= 12.0 ? 16 : 32; }
 
 template <int KIND, int MODE, int TG>
 static hipError_t launch_mid(const GemmArgs& a, hipStream_t s) {
@@ -557,7 +561,7 @@ static hipError_t launch_mid4_cbw(const GemmArgs& a, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const unsigned gx = (unsigned)(n < 65536 ? n : 65536);
     const unsigned gy = (unsigned)((n + gx - 1) / gx);
-    hipLaunchKernelGGL((mid4_gemm_kernel<KIND, CBW>), dim3(gx, gy), dim3(64 * kMidWaves), lds, s, a);
+    hipLaunchKernelGGL((mid4_gemm_kernel<KIND, CBW>), dim3(gx, gy), dim3(64 * kMid4Waves), lds, s, a);
     return hipGetLastError();
 }
 
@@ -571,12 +575,16 @@ static hipError_t launch_mid4(const GemmArgs& a, hipStream_t s) {
 // packed (W4A4 with NVFP4 activations): mid4 kernels; else 16-bit activations
 hipError_t launch_mid_gemm1(const GemmArgs& a, hipStream_t s) {
     if (a.packed) return launch_mid4<1>(a, s);
-    return a.mode == 0 ? launch_mid<1, 0, kMidTG>(a, s) : launch_mid<1, 1, kMidTG>(a, s);
+    if (mid_rows(a.T, a.topk, a.E) == 16)
+        return a.mode == 0 ? launch_mid<1, 0, 1>(a, s) : launch_mid<1, 1, 1>(a, s);
+    return a.mode == 0 ? launch_mid<1, 0, 2>(a, s) : launch_mid<1, 1, 2>(a, s);
 }
 
 hipError_t launch_mid_gemm2(const GemmArgs& a, hipStream_t s) {
     if (a.packed) return launch_mid4<2>(a, s);
-    return a.mode == 0 ? launch_mid<2, 0, kMidTG>(a, s) : launch_mid<2, 1, kMidTG>(a, s);
+    if (mid_rows(a.T, a.topk, a.E) == 16)
+        return a.mode == 0 ? launch_mid<2, 0, 1>(a, s) : launch_mid<2, 1, 1>(a, s);
+    return a.mode == 0 ? launch_mid<2, 0, 2>(a, s) : launch_mid<2, 1, 2>(a, s);
 }
 
 }  // namespace moe

@@ -92,20 +92,25 @@ def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
 
 def test_resolved_path_crossover():
     # expected local pairs per local expert T*k/E: W4A16 streams with the
-    # block-diagonal kernels up to 5.5, with the dense ones up to 22 (d % 256
-    # == 0), then tiles; packed W4A4 streams up to 6; W4A4 whose d or F is not
-    # a multiple of 256 streams up to 9
+    # block-diagonal kernels up to 4.6, with the dense ones up to 44 (d % 256
+    # == 0), then tiles; W4A4 with NVFP4 activations (d, F multiples of 256, at
+    # most 8192) up to 5 and 18; larger packed W4A4 streams up to 6; W4A4 whose
+    # d or F is not a multiple of 256 streams up to 9
     def path(T, mode, d=4096, F=1024, force=nv.PATH_AUTO):
         return nv.moe_nvfp4_resolved_path(nv.make_problem(T, d, F, 320, 8, 0, 160, True, mode, force))
     assert path(64, nv.W4A16) == nv.PATH_DECODE
-    assert path(220, nv.W4A16) == nv.PATH_DECODE          # 5.5
-    assert path(221, nv.W4A16) == nv.PATH_MID
-    assert path(880, nv.W4A16) == nv.PATH_MID             # 22.0
-    assert path(881, nv.W4A16) == nv.PATH_PREFILL
+    assert path(184, nv.W4A16) == nv.PATH_DECODE          # 4.6
+    assert path(185, nv.W4A16) == nv.PATH_MID
+    assert path(1760, nv.W4A16) == nv.PATH_MID            # 44.0
+    assert path(1761, nv.W4A16) == nv.PATH_PREFILL
     assert path(360, nv.W4A16, d=3968) == nv.PATH_DECODE  # d % 256 != 0: no dense path, threshold 9
     assert path(361, nv.W4A16, d=3968) == nv.PATH_PREFILL
-    assert path(240, nv.W4A4) == nv.PATH_DECODE           # 6.0
-    assert path(241, nv.W4A4) == nv.PATH_PREFILL
+    assert path(200, nv.W4A4) == nv.PATH_DECODE           # 5.0
+    assert path(201, nv.W4A4) == nv.PATH_MID
+    assert path(720, nv.W4A4) == nv.PATH_MID              # 18.0
+    assert path(721, nv.W4A4) == nv.PATH_PREFILL
+    assert path(240, nv.W4A4, d=16384) == nv.PATH_DECODE  # packed, beyond the dense path's 8192: 6.0
+    assert path(241, nv.W4A4, d=16384) == nv.PATH_PREFILL
     assert path(300, nv.W4A4, F=384) == nv.PATH_DECODE    # not packed: threshold 9
     assert path(8192, nv.W4A16, force=nv.PATH_DECODE) == nv.PATH_DECODE
     assert path(1, nv.W4A4, force=nv.PATH_PREFILL) == nv.PATH_PREFILL
@@ -128,7 +133,7 @@ def test_static_globals_are_validated():
     # the static mode resolves its path like W4A4 and needs the same workspace
     ps = nv.make_problem(300, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4_STATIC, nv.PATH_AUTO, (0.01, 0.01))
     pd = nv.make_problem(300, 4096, 1024, 320, 8, 0, 160, True, nv.W4A4)
-    assert nv.moe_nvfp4_resolved_path(ps) == nv.moe_nvfp4_resolved_path(pd) == nv.PATH_PREFILL
+    assert nv.moe_nvfp4_resolved_path(ps) == nv.moe_nvfp4_resolved_path(pd) == nv.PATH_MID
     assert nv.moe_nvfp4_workspace_size(ps) == nv.moe_nvfp4_workspace_size(pd)
 
 

@@ -259,11 +259,12 @@ def test_full_size_two_shards_sum_to_unsharded_oracle():
 
 
 @pytest.mark.parametrize("mode", [W4A16, W4A4])
-@pytest.mark.parametrize("T", [1, 15, 16, 17, 200])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 100, 200])
 def test_mid_path_tile_edges(T, mode):
-    """The dense weight-streaming path on 16-row tiles: one token, one short of
-    a tile, exactly a tile, one past it (an expert with two tiles), and many
-    tiles per expert; whole output."""
+    """The dense weight-streaming path: on 16-row tiles (up to 12 expected pairs
+    per expert) one token, one short of a tile, exactly a tile and one past it
+    (an expert with two tiles); on 32-row tiles about half a tile per expert and
+    more than a tile per expert; whole output."""
     require_gpu()
     lay = layer("mid", T=T)
     w = lay.w
