@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_nvfp4.so")
-SOURCES = ["router.hip", "quant.hip", "gemm.hip", "prefill.hip", "decode.hip", "mid.hip", "tile32.hip", "engine.cpp"]
+SOURCES = ["router.hip", "quant.hip", "gemm.hip", "prefill.hip", "decode.hip", "mid.hip", "engine.cpp"]
 ARCH = "gfx950"
 
 

@@ -126,10 +126,6 @@ int mid_rows(int T, int topk, int E);             // rows per tile of the dense 
 int mid_rows_packed();                            // ... with W4A4 activations as NVFP4
 hipError_t launch_mid_gemm1(const GemmArgs& a, hipStream_t s);
 hipError_t launch_mid_gemm2(const GemmArgs& a, hipStream_t s);
-bool t32_ok(int d, int F);                        // 32-row tiles with the deep LDS weight ring apply
-int t32_rows();                                   // rows per tile of those kernels
-hipError_t launch_t32_gemm1(const GemmArgs& a, hipStream_t s);
-hipError_t launch_t32_gemm2(const GemmArgs& a, hipStream_t s);
 
 // Raise kernel Kern's dynamic-LDS limit to `bytes` on the current device when
 // that is above the 64 KB default; the attribute is per device, so the largest
