@@ -392,8 +392,10 @@ bool pf_packed_ok(int d, int F) { return d % kQK == 0 && F % kQK == 0; }
 
 template <int KIND, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
-    constexpr int WN = WAVES / 2;                  // waves along the weight rows
-    constexpr int NJ = kPN / WN / 32;              // 32-column blocks per wave (2 or 4)
+    constexpr int WN = 4;                          // waves along the weight rows
+    constexpr int WM = WAVES / WN;                 // waves along the tile rows (2 or 4)
+    constexpr int NVM = kPM / (32 * WM);           // 32-row blocks per wave (4 or 2)
+    constexpr int NJ = kPN / WN / 32;              // 32-column blocks per wave
     constexpr int NQ = 32 / WAVES;                 // code loads per operand, wave and chunk
     constexpr int SR = 256 / WAVES;                // scale rows per wave (lanes)
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
     const uint8_t* bss = wscales + (size_t)weight_row(sr) * (K / 16);
     const float gscale = KIND == 1 ? W.g13[ex] * a.a1g : W.g2[ex] * a.a2g;   // weight x activation globals
 
-    const int nvi = max(0, min(4, (re - rb - wm * 128 + 31) >> 5));
+    const int nvi = max(0, min(NVM, (re - rb - wm * (32 * NVM) + 31) >> 5));
     const int nc = K / kQK;
 
     auto issue = [&](int c, int slot) {
@@ -472,9 +474,9 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
         }
     };
 
-    f32x16_t acc[4][NJ];
+    f32x16_t acc[NVM][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NVM; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -487,15 +489,15 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
         brow[j] = (KIND == 1 ? (j < NJ / 2 ? wn * 16 * NJ + j * 32 : 128 + wn * 16 * NJ + (j - NJ / 2) * 32)
                              : wn * 32 * NJ + j * 32) +
                   (lane & 31);
-    const int arow0 = wm * 128 + (lane & 31);
+    const int arow0 = wm * (32 * NVM) + (lane & 31);
 
     // one step (64 k) of a chunk: lane half h of MFMA kk takes k = 32h + 8kk ..
     // +8 of the step: dword kk of the row's 16-byte code unit 2s + h, scale byte
     // 2h + kk/2 of the step's 4
     auto step = [&](auto nv_c, const uint8_t* S, int s) {
         constexpr int NV = decltype(nv_c)::value;
-        u32x4_t ac[4], bc[NJ];
-        uint32_t as[4], bs[NJ];
+        u32x4_t ac[NVM], bc[NJ];
+        uint32_t as[NVM], bs[NJ];
         static_assert(NJ <= 4, "operand blocks");
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -509,14 +511,14 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
             bs[j] = *reinterpret_cast<const uint32_t*>(S + 2 * kQCodes + kQScales + brow[j] * 16 + s * 4) >> (16 * h);
         }
         // the lane half's two block scales of the step, as f16 {MFMAs 0-1, 2-3}
-        f16x2_t asc[4], bsc[NJ];
+        f16x2_t asc[NVM], bsc[NJ];
 #pragma unroll
         for (int i = 0; i < NV; ++i) asc[i] = e4m3x2_to_f16(as[i]);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bsc[j] = e4m3x2_to_f16(bs[j]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            u32x4_t av[4], bv[NJ];
+            u32x4_t av[NVM], bv[NJ];
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const _Float16 sc = kk < 2 ? bsc[j].x : bsc[j].y;
@@ -552,8 +554,8 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
     issue(0, 0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     switch (nvi) {
-        case 4: kloop(std::integral_constant<int, 4>{}); break;
-        case 3: kloop(std::integral_constant<int, 3>{}); break;
+        case 4: if constexpr (NVM >= 4) kloop(std::integral_constant<int, 4>{}); break;
+        case 3: if constexpr (NVM >= 3) kloop(std::integral_constant<int, 3>{}); break;
         case 2: kloop(std::integral_constant<int, 2>{}); break;
         case 1: kloop(std::integral_constant<int, 1>{}); break;
         default: kloop(std::integral_constant<int, 0>{}); break;
@@ -566,14 +568,14 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
         constexpr int ES = 136;
         float* E = reinterpret_cast<float*>(smem);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NVM; ++i) {
             if (i >= nvi) break;
 #pragma unroll
             for (int j = 0; j < NJ / 2; ++j) {
                 const int col = wn * 16 * NJ + j * 32 + (lane & 31);
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                    const int row = wm * (32 * NVM) + i * 32 + (v >> 2) * 8 + lr + (v & 3);
                     E[row * ES + col] = silu_fast(acc[i][j][v] * gscale) * (acc[i][j + NJ / 2][v] * gscale);
                 }
             }
@@ -610,14 +612,14 @@ __global__ __launch_bounds__(64 * WAVES) void pf4_gemm_kernel(GemmArgs a) {
     constexpr int YS = 264;
     uint16_t* Ys = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NVM; ++i) {
         if (i >= nvi) break;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int col = wn * 32 * NJ + j * 32 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = wm * 128 + i * 32 + (v >> 2) * 8 + lr + (v & 3);
+                const int row = wm * (32 * NVM) + i * 32 + (v >> 2) * 8 + lr + (v & 3);
                 Ys[row * YS + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * gscale);
             }
         }

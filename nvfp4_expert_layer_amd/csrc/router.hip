@@ -39,15 +39,19 @@ namespace moe {
 constexpr int kR1Tile = 64;     // tokens x experts per workgroup
 constexpr int kR1BK = 64;
 constexpr int kR1Pad = 8;       // bf16 elements of row padding in LDS
+constexpr int kR1Depth = 4;     // K chunks of loads in flight per workgroup
 
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, int T, int E, int d,
     int kslice, float* __restrict__ part, double* __restrict__ xn2, double* __restrict__ gn2) {
-    // double-buffered LDS tiles: the next K chunk is loaded while this one runs on MFMA
+    // double-buffered LDS tiles, fed from a register ring that keeps the loads
+    // of the next kR1Depth chunks in flight (the chunks come mostly from L2,
+    // and one chunk of MFMA work is far shorter than an L2 round trip)
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][kR1Tile][kR1BK + kR1Pad];
     __shared__ __attribute__((aligned(16))) uint16_t gs[2][kR1Tile][kR1BK + kR1Pad];
     const int t0 = blockIdx.x * kR1Tile, e0 = blockIdx.y * kR1Tile, ks = blockIdx.z;
     const int kbeg = ks * kslice, kend = min(d, kbeg + kslice);
+    const int nchunk = kend > kbeg ? (kend - kbeg) / kR1BK : 0;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // wave layout 2x2: wave (wm, wn) owns tokens [32 wm, +32) x experts [32 wn, +32)
     const int wm = wave >> 1, wn = wave & 1;
@@ -56,26 +60,31 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // 64 rows x 64 bf16 of X and of G per chunk: 512 16-byte pieces each, 2 per thread
-    u32x4_t vx[2], vg[2];
-    auto load = [&](int k0) {
+    // 64 rows x 64 bf16 of X and of G per chunk: 512 16-byte pieces each, 2 per
+    // thread; rows past T or E read row 0 of the tile (discarded at the end)
+    const int r0 = tid >> 3, cc = (tid & 7) * 8;
+    const uint16_t* xsrc[2];
+    const uint16_t* gsrc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int r = r0 + 32 * c;
+        xsrc[c] = X + (size_t)(t0 + (t0 + r < T ? r : 0)) * d + cc;
+        gsrc[c] = G + (size_t)(e0 + (e0 + r < E ? r : 0)) * d + cc;
+    }
+    u32x4_t vx[kR1Depth][2], vg[kR1Depth][2];
+    auto load = [&](int ci, u32x4_t (&x)[2], u32x4_t (&g)[2]) {
+        const int k0 = kbeg + min(ci, nchunk - 1) * kR1BK;   // past the end: re-load the last chunk
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int chunk = tid + c * 256;
-            const int r = chunk >> 3, cc = (chunk & 7) * 8;
-            vx[c] = u32x4_t{0u, 0u, 0u, 0u};
-            vg[c] = u32x4_t{0u, 0u, 0u, 0u};
-            if (t0 + r < T) vx[c] = *reinterpret_cast<const u32x4_t*>(X + (size_t)(t0 + r) * d + k0 + cc);
-            if (e0 + r < E) vg[c] = *reinterpret_cast<const u32x4_t*>(G + (size_t)(e0 + r) * d + k0 + cc);
+            x[c] = *reinterpret_cast<const u32x4_t*>(xsrc[c] + k0);
+            g[c] = *reinterpret_cast<const u32x4_t*>(gsrc[c] + k0);
         }
     };
-    auto store = [&](int b) {
+    auto store = [&](int b, const u32x4_t (&x)[2], const u32x4_t (&g)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int chunk = tid + c * 256;
-            const int r = chunk >> 3, cc = (chunk & 7) * 8;
-            *reinterpret_cast<u32x4_t*>(&xs[b][r][cc]) = vx[c];
-            *reinterpret_cast<u32x4_t*>(&gs[b][r][cc]) = vg[c];
+            *reinterpret_cast<u32x4_t*>(&xs[b][r0 + 32 * c][cc]) = x[c];
+            *reinterpret_cast<u32x4_t*>(&gs[b][r0 + 32 * c][cc]) = g[c];
         }
     };
     // squared norms (token rows in the first expert tile, expert rows in the
@@ -84,15 +93,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
     double nx[2] = {0.0, 0.0}, ng[2] = {0.0, 0.0};
     const bool want_x = blockIdx.y == 0, want_g = blockIdx.x == 0;
     const int nrow = tid >> 2, nq = (tid & 3) * 16;
-    if (kbeg < kend) {
-        load(kbeg);
-        store(0);
-    }
-    __syncthreads();
-    int b = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += kR1BK) {
-        const bool more = k0 + kR1BK < kend;
-        if (more) load(k0 + kR1BK);
+    auto chunk = [&](int b) {
         auto sq16 = [&](const uint16_t* row, double (&acc)[2]) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(row);
             const u32x4_t c = *reinterpret_cast<const u32x4_t*>(row + 8);
@@ -121,9 +122,27 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
         }
-        if (more) store(b ^ 1);
+    };
+    if (nchunk > 0) {
+        // ring slot u holds chunk u + kR1Depth * round; chunk 0 goes to LDS first
+#pragma unroll
+        for (int u = 0; u < kR1Depth; ++u) load(u, vx[u], vg[u]);
+        store(0, vx[0], vg[0]);
+        load(kR1Depth, vx[0], vg[0]);
         __syncthreads();
-        b ^= 1;
+        // whole ring rounds (chunks past the end re-load the last chunk and
+        // are not multiplied)
+        for (int c0 = 0; c0 < nchunk; c0 += kR1Depth) {
+#pragma unroll
+            for (int u = 0; u < kR1Depth; ++u) {
+                const int c = c0 + u;                          // chunk in LDS buffer c & 1
+                if (c < nchunk) chunk(c & 1);
+                const int un = (u + 1) % kR1Depth;             // slot of chunk c + 1
+                if (c + 1 < nchunk) store((c + 1) & 1, vx[un], vg[un]);
+                load(c + 1 + kR1Depth, vx[un], vg[un]);
+                __syncthreads();
+            }
+        }
     }
     float* out = part + (size_t)ks * T * E;
 #pragma unroll
