@@ -58,6 +58,7 @@ STAGES = ["route_permute", "act_quant", "gemm1_swiglu", "gemm2", "combine"]
 G1_EVERY = 4                    # timed steps per GEMM1 event pair
 PREWARM_S = 0.3                 # untimed forward calls before the warm-up steps (clock settling)
 CSRC = os.path.join(ROOT, "nvfp4_expert_layer_amd", "csrc")
+from nvfp4_expert_layer_amd.build import EXTRA_FLAGS as BUILD_FLAGS   # noqa: E402  (plain dict, no compilation)
 # sources whose machine code the dominant kernel of each path is built from
 KERNEL_SOURCES = {"decode": ["decode.hip", "device_common.h", "kernels.h"],
                   "mid": ["mid.hip", "device_common.h", "kernels.h"],
@@ -80,6 +81,7 @@ def kernel_source_hash(path):
         t = re.sub(r"//[^\n]*", "", t)
         t = " ".join(t.split())                                # nor does layout
         h.update(t.encode())
+    h.update(" ".join(BUILD_FLAGS.get(KERNEL_SOURCES[path][0], [])).encode())   # per-source compiler options
     return h.hexdigest()[:16]
 
 

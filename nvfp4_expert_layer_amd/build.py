@@ -34,9 +34,17 @@ def _flags():
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
+# Per-source compiler options.  The tiled GEMMs are scheduled for instruction
+# level parallelism (LLVM's max-ilp machine scheduler): measured 4% faster on
+# the T=8192 W4A4 layer's GEMMs (GEMM1 1229 against 1284 us, GEMM2 634 against
+# 672 us), 1% on the T=16384 W4A16 shard; the other sources measured equal or
+# slower with it.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + _flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + _flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
