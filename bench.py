@@ -107,6 +107,76 @@ def measured_traffic(path, workload):
         return None
 
 
+def prewarm(call):
+    """Untimed calls for PREWARM_S seconds (the GPU's clocks settle under load);
+    returns how many ran."""
+    t_end = time.perf_counter() + PREWARM_S
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            call()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+GRAPH_PROBE_CALLS = 50
+
+
+def graph_probe(name):
+    """GRAPH_PROBE_CALLS direct forward calls, then the same forward captured in
+    a HIP graph and replayed 5 + GRAPH_PROBE_CALLS times, for a kernel trace
+    that compares the two (see --trace-summary).  Prints both wall times."""
+    w = workloads.WORKLOADS[name]
+    local, shared = build_weights(w)
+    gate_w = workloads.gen_gate(w, "cuda").t().contiguous()
+    x = workloads.gen_hidden(w, "cuda")
+    p = nv.make_problem(w.T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, w.mode, nv.PATH_AUTO, w.act_global)
+    ws = nv.alloc_workspace(p)
+    out = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
+    prewarm(lambda: nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out))
+    t0 = time.perf_counter()
+    for _ in range(GRAPH_PROBE_CALLS):
+        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+    torch.cuda.synchronize()
+    direct = (time.perf_counter() - t0) / GRAPH_PROBE_CALLS
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(GRAPH_PROBE_CALLS):
+        graph.replay()
+    torch.cuda.synchronize()
+    replay = (time.perf_counter() - t0) / GRAPH_PROBE_CALLS
+    print(json.dumps({"workload": name, "direct_us": round(direct * 1e6, 1), "graph_replay_us": round(replay * 1e6, 1),
+                      "calls": GRAPH_PROBE_CALLS}))
+
+
+def trace_summary(csv_path, per_call):
+    """Per-kernel average durations and the mean gap between kernels in the two
+    phases of a --graph-probe run, from rocprofv3's kernel_trace.csv: the last
+    GRAPH_PROBE_CALLS forwards are graph replays, the GRAPH_PROBE_CALLS before
+    the 5 unmeasured replays are direct calls (per_call kernels a forward)."""
+    import csv
+    import collections
+    rows = [r for r in csv.DictReader(open(csv_path)) if "moe::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    n, c = len(rows), per_call * GRAPH_PROBE_CALLS
+    phases = {"direct": rows[n - 2 * c - 5 * per_call: n - c - 5 * per_call], "graph_replay": rows[n - c:]}
+    for label, ph in phases.items():
+        d = collections.OrderedDict()
+        for r in ph:
+            d.setdefault(r["Kernel_Name"][:60], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        span = (int(ph[-1]["End_Timestamp"]) - int(ph[0]["Start_Timestamp"])) / 1e3 / GRAPH_PROBE_CALLS
+        gaps = [(int(ph[i + 1]["Start_Timestamp"]) - int(ph[i]["End_Timestamp"])) / 1e3 for i in range(len(ph) - 1)]
+        print(f"{label}: {span:.1f} us per forward, mean gap between kernels {sum(gaps) / len(gaps):.2f} us")
+        for k, v in d.items():
+            print(f"   {k:60s} {sum(v) / len(v):9.2f} us  ({len(v)} calls)")
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain copy of known size in one elementwise kernel (y = x + 0, so that
     it is a kernel dispatch and not a DMA blit), for scaling the FETCH_SIZE /
@@ -208,13 +278,7 @@ def bench_workload(name, steps, warmup, hip):
     # pre-warm (untimed): the GPU's clocks need ~0.1-0.2 s of load to settle; at
     # T=64 twenty steps right after set-up measured 409 us/step, 222 after 20
     # more, 217 after 200 (the per-call median is the same in each)
-    t_end = time.perf_counter() + PREWARM_S
-    prewarm_calls = 0
-    while time.perf_counter() < t_end:
-        for _ in range(10):
-            nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
-        prewarm_calls += 10
-        torch.cuda.synchronize()
+    prewarm_calls = prewarm(lambda: nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out))
     for _ in range(warmup):
         nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
     # timed region: K steps.  The dominant kernel's duration is measured live:
@@ -400,9 +464,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel source hashes and exit")
+    ap.add_argument("--graph-probe", action="store_true",
+                    help="only run direct calls, then graph replays, of --workload (for a kernel trace) and exit")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarise rocprofv3's kernel trace of a --graph-probe run and exit")
+    ap.add_argument("--kernels-per-call", type=int, default=6, help="kernels of one forward (--trace-summary)")
     args = ap.parse_args()
     if args.source_hash:
         print(json.dumps({p: kernel_source_hash(p) for p in KERNEL_SOURCES}))
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.kernels_per_call)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this layer runs on one GPU: the expert shard is exercised by running one "
@@ -418,6 +490,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.graph_probe:
+        graph_probe(args.workload)
         return
     nv.lib()
     hip = HipEvents()
