@@ -245,6 +245,8 @@ int run_route(const moe_nvfp4_problem& p, const Plan& pl, const void* hidden, co
     q.offsets = offsets_out ? offsets_out : at<int32_t>(ws, pl.offsets);
     q.tiles = at<int4>(ws, pl.tiles); q.ntiles = at<int32_t>(ws, pl.ntiles);
     q.perm = perm_out ? perm_out : at<int32_t>(ws, pl.perm); q.inv = at<int32_t>(ws, pl.inv);
+    if (pl.exact && moe::route_fused_ok(r.T, r.E, r.d, r.L))
+        return hip_status(moe::launch_route_exact_fused(r, q, s), "router launch");
     int st = hip_status(pl.exact ? moe::launch_route_exact(r, s) : moe::launch_router(r, s), "router launch");
     if (st) return st;
     return hip_status(moe::launch_permute(q, s), "permutation launch");

@@ -97,6 +97,9 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 bool router_exact(int T, int E, int d);           // exact fp64 logits for this batch
 int router_exact_ksplit(int T, int E, int d);
 hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s);
+// few tokens: exact logits, then selection and permutation in one launch
+bool route_fused_ok(int T, int E, int d, int L);
+hipError_t launch_route_exact_fused(const RouterArgs& a, const PermArgs& q, hipStream_t s);
 hipError_t launch_permute(const PermArgs& a, hipStream_t s);
 hipError_t launch_quantize_act(const uint16_t* x, int R, int C, float g, uint8_t* codes, uint8_t* scales,
                                hipStream_t s);

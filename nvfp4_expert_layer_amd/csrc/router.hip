@@ -928,6 +928,99 @@ __global__ __launch_bounds__(1024) void router_exact_select_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// At most kFuseTokens tokens and kFuseItems (token, expert) logits: the exact
+// selection and the permutation in one workgroup (one launch after the logits
+// instead of two).  The T x E logits are the slice partials added in slice
+// order, as in router_exact_select_kernel (two items' loads in flight per
+// thread), kept in LDS; wave t then selects for token t exactly as that
+// kernel's wave 0 does; then the whole workgroup runs the permutation of
+// perm_small_kernel.  One CU then reads all T x E x (K slices) partials, so the
+// fusion pays only while they are few.  Measured on the 320-expert shard
+// (routing stage time, 16 K slices): T = 1 15.7 -> 14.5 us, T = 2 15.9 -> 15.3;
+// T = 6 16.5 -> 18.1 and T = 16 17.3 -> 26.1 (slower); on the 16-expert layer
+// (one K slice) at T = 16: 13.3 -> 12.4 us.
+// ---------------------------------------------------------------------------
+constexpr int kFuseTokens = 16;
+constexpr int kFuseItems = 640;             // token-expert logits
+
+template <int EPL>
+__global__ __launch_bounds__(1024) void router_exact_finish_kernel(RouterArgs r, PermArgs q) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char fl[];
+    double* const s_val = reinterpret_cast<double*>(fl);                              // [T][E]
+    uint32_t* const masks = reinterpret_cast<uint32_t*>(fl + (size_t)r.T * r.E * 8);   // [L][ceil(T/32)]
+    __shared__ int32_t s_id[kFuseTokens][32];
+    __shared__ double s_sc[kFuseTokens][32];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = r.T, E = r.E, KS = r.KS, topk = r.topk;
+    const int n = T * E;
+    for (int i0 = tid; i0 < n; i0 += 2048) {
+        double pv[2][kMaxKS];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = min(i0 + h * 1024, n - 1);
+            const int t = i / E, e = i - t * E;
+#pragma unroll
+            for (int sl = 0; sl < kMaxKS; ++sl) pv[h][sl] = r.xpart[((size_t)min(sl, KS - 1) * T + t) * E + e];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = i0 + h * 1024;
+            if (i < n) {
+                double v = pv[h][0];
+#pragma unroll
+                for (int sl = 1; sl < kMaxKS; ++sl)
+                    if (sl < KS) v += pv[h][sl];
+                s_val[i] = v;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave < T) {
+        const int t = wave;
+        const double* val = s_val + (size_t)t * E;
+        uint64_t key[EPL];
+#pragma unroll
+        for (int sl = 0; sl < EPL; ++sl) {
+            const int e = lane + 64 * sl;
+            key[sl] = e < E ? f64_key(val[e]) : 0ull;
+        }
+        for (int rr = 0; rr < topk; ++rr) {
+            uint64_t m = 0;
+#pragma unroll
+            for (int sl = 0; sl < EPL; ++sl) m = key[sl] > m ? key[sl] : m;
+            const uint64_t M = wave_max_u64(m);
+            uint32_t c = 0;                              // 0xFFFFFFFF - id: the max is the lowest id
+#pragma unroll
+            for (int sl = EPL - 1; sl >= 0; --sl)
+                if (key[sl] == M) c = 0xFFFFFFFFu - (uint32_t)(lane + 64 * sl);
+            const int id = (int)(0xFFFFFFFFu - wave_max_u32(c));
+#pragma unroll
+            for (int sl = 0; sl < EPL; ++sl)
+                if (lane + 64 * sl == id) key[sl] = 0;
+            if (lane == 0) {
+                s_id[t][rr] = id;
+                s_sc[t][rr] = val[id];
+            }
+        }
+        __builtin_amdgcn_wave_barrier();                 // (a wave's LDS accesses complete in order)
+        const double my = lane < topk ? s_sc[t][lane] : 0.0;
+        const double z = lane < topk ? exp(my - s_sc[t][0]) : 0.0;
+        const double zs = wave_sum_f64(z);
+        if (lane < topk) {
+            const int my_id = s_id[t][lane];
+            const size_t o = (size_t)t * topk + lane;
+            r.topk_ids[o] = my_id;
+            r.topk_w[o] = (float)(z / zs);
+            const int lam = my_id - r.offset;
+            r.local_ids[o] = (lam >= 0 && lam < r.L) ? lam : -1;
+        }
+    }
+    __syncthreads();                                     // the local ids are visible to the workgroup
+    perm_small_body(q.local_ids, T, topk, q.L, q.has_shared, q.BM, q.counts, q.offsets, q.tiles, q.ntiles,
+                    q.max_tiles, q.perm, q.inv, masks);
+}
+
+// ---------------------------------------------------------------------------
 // P3: scatter pair ids into the permutation; inverse map pair -> row (-1 dropped).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -1006,7 +1099,7 @@ int router_exact_ksplit(int T, int E, int d) {
     return ks < 1 ? 1 : ks;
 }
 
-hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
+static hipError_t launch_exact_logits(const RouterArgs& a, hipStream_t s) {
     if (!router_exact(a.T, a.E, a.d) || a.KS < 1 || a.KS > kMaxKS) return hipErrorInvalidValue;
     constexpr int W = kXWaves;
     const int kslice = ((a.d + a.KS - 1) / a.KS + 32 * W - 1) / (32 * W) * (32 * W);
@@ -1021,12 +1114,41 @@ hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
     else
         hipLaunchKernelGGL((router_exact_logits_kernel<kXMaxTG, W>), g1, dim3(64 * W), 0, s, a.X, a.G, a.T, a.E, a.d,
                            kslice, a.xpart);
+    return hipSuccess;
+}
+
+hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
+    const hipError_t e = launch_exact_logits(a, s);
+    if (e != hipSuccess) return e;
     auto k = a.E <= 128 ? router_exact_select_kernel<2>
              : a.E <= 320 ? router_exact_select_kernel<5>
              : a.E <= 512 ? router_exact_select_kernel<8>
                           : router_exact_select_kernel<kMaxExperts / 64>;
     hipLaunchKernelGGL(k, dim3(a.T), dim3(1024), 0, s, a.xpart, a.T, a.E, a.KS, a.topk, a.offset, a.L, a.topk_ids,
                        a.topk_w, a.local_ids);
+    return hipGetLastError();
+}
+
+static size_t route_fused_lds(int T, int E, int L) {
+    return (size_t)T * E * 8 + (size_t)L * ((T + 31) / 32) * 4;
+}
+
+bool route_fused_ok(int T, int E, int d, int L) {
+    return router_exact(T, E, d) && T <= kFuseTokens && T * E <= kFuseItems && L <= 1024 &&
+           route_fused_lds(T, E, L) <= 65536;
+}
+
+hipError_t launch_route_exact_fused(const RouterArgs& a, const PermArgs& q, hipStream_t s) {
+    if (!route_fused_ok(a.T, a.E, a.d, a.L) || q.T != a.T || q.L != a.L || q.topk != a.topk ||
+        q.local_ids != a.local_ids)
+        return hipErrorInvalidValue;
+    const hipError_t e = launch_exact_logits(a, s);
+    if (e != hipSuccess) return e;
+    auto k = a.E <= 128 ? router_exact_finish_kernel<2>
+             : a.E <= 320 ? router_exact_finish_kernel<5>
+             : a.E <= 512 ? router_exact_finish_kernel<8>
+                          : router_exact_finish_kernel<kMaxExperts / 64>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(1024), route_fused_lds(a.T, a.E, a.L), s, a, q);
     return hipGetLastError();
 }
 

@@ -119,11 +119,13 @@ def test_route_empty_batch():
     assert not counts.any().item() and not offsets.any().item()
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 16, 17, 33, 64, 65, 128, 129])
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 16, 17, 33, 64, 65, 128, 129])
 def test_route_few_tokens_both_sides_of_the_exact_fp64_path(T):
     """Up to 128 tokens the logits are computed exactly in fp64 on the matrix
     cores (no bounds, no re-scoring; token tiles of 16, 32 and 64 rows, full and
-    ragged); 129 tokens take the certified bf16-MFMA path."""
+    ragged); up to 2 tokens (640 token-expert logits) the selection and the
+    permutation then run in one workgroup, from 3 in a workgroup per token and a
+    permutation launch; 129 tokens take the certified bf16-MFMA path."""
     require_gpu()
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     log(f"route few tokens T={T}")
