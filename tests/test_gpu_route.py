@@ -77,7 +77,7 @@ def test_route_zero_tokens_tie_to_lowest_ids():
 
 
 def test_route_wide_select_zero_tokens_and_shard():
-    """T >= 1024 takes the one-wave-per-token selection: zero tokens (every expert
+    """T >= 512 takes the one-wave-per-token selection: zero tokens (every expert
     a candidate) and a shard filter, against the oracle."""
     require_gpu()
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=1100)
