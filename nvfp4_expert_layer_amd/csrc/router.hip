@@ -187,6 +187,12 @@ constexpr int kSelThreads = 1024;
 // layer, workgroup per token against wave per token: T = 129 30.6 / 42.6 us,
 // T = 256 33.6 / 45.0, T = 512 53.2 / 50.9, T = 768 66.0 / 54.2.
 constexpr int kWideSelectTokens = 512;
+// Below kSplitSelectTokens the four waves of a workgroup share each token's K
+// chunks.  Routing stage time on the 320-expert layer, one wave against four
+// per token: T = 512 ~51 / 46.5 us, T = 768 54.2 / 53.2; T = 1024 56.8 / 64.6
+// (four slower).  Against the workgroup per token below 512: T = 129 30.6 /
+// 33.7, T = 256 33.5 / 35.9.
+constexpr int kSplitSelectTokens = 1024;
 
 // Wave-wide unsigned max through DPP row shifts and row broadcasts (lanes that
 // read outside their row get 0, the identity): after the row_shr steps lane 15
@@ -405,19 +411,29 @@ __global__ __launch_bounds__(kSelThreads) void router_select_kernel(
 constexpr int kWTok = 4;            // tokens (waves) per workgroup
 constexpr int kWGroup = 8;          // candidates scored together
 
-template <int kWSlots>
+// WPT waves per token (1, or kWTok: the workgroup's waves share one token).
+// With several, every wave of the token computes the same bounds and candidate
+// list, each re-scores its own share of the K chunks, and the shares' sums are
+// added in wave order; one wave then ranks.  A token's latency is a chain of
+// dependent round trips (the candidates' chunks above all), which the split
+// shortens where few tokens leave the chip idle.
+template <int kWSlots, int WPT>
 __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
     int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ local_ids) {
+    static_assert(WPT == 1 || WPT == kWTok, "one token per wave or per workgroup");
     __shared__ int32_t s_cid[kWTok][kMaxExperts];
     __shared__ double s_csc[kWTok][kMaxExperts];
     __shared__ int32_t s_sel_id[kWTok][32];
     __shared__ double s_sel_sc[kWTok][32];
+    __shared__ double s_share[WPT > 1 ? WPT : 1][kWGroup];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int t = blockIdx.x * kWTok + w;
-    if (t >= T) return;                                  // whole wave; no workgroup barriers below
+    const int sub = w % WPT;                             // this wave's share of the token's K chunks
+    const int t = blockIdx.x * (kWTok / WPT) + w / WPT;
+    // whole wave (WPT == 1: no workgroup barriers below), or whole workgroup
+    if (t >= T) return;
     int32_t* cid = s_cid[w];
     double* csc = s_csc[w];
 
@@ -506,6 +522,10 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
     // software-pipelined (the next 512-element chunk's loads go out before
     // this chunk is multiplied); a short last group skips its empty slots ----
     const uint16_t* xrow = X + (size_t)t * d;
+    // this wave's chunks of 512 elements: [c_lo, c_hi)
+    const int nchunk = (d + 511) / 512;
+    const int c_lo = sub * nchunk / WPT, c_hi = (sub + 1) * nchunk / WPT;
+    const int k_end = min(d, 512 * c_hi);
     for (int g0 = 0; g0 < nc; g0 += kWGroup) {
         const int ng = min(kWGroup, nc - g0);
         const uint16_t* grow[kWGroup];
@@ -514,20 +534,20 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
         double acc[kWGroup];
 #pragma unroll
         for (int c = 0; c < kWGroup; ++c) acc[c] = 0.0;
-        int k0 = lane * 8;
+        int k0 = 512 * c_lo + lane * 8;
         u32x4_t xv{0u, 0u, 0u, 0u}, gv[kWGroup];
-        if (k0 < d) {
+        if (k0 < k_end) {
             xv = *reinterpret_cast<const u32x4_t*>(xrow + k0);
 #pragma unroll
             for (int c = 0; c < kWGroup; ++c)
                 if (c < ng) gv[c] = *reinterpret_cast<const u32x4_t*>(grow[c] + k0);
         }
-        for (; k0 < d; k0 += 512) {
+        for (; k0 < k_end; k0 += 512) {
             const u32x4_t xc = xv;
             u32x4_t gc[kWGroup];
 #pragma unroll
             for (int c = 0; c < kWGroup; ++c) gc[c] = gv[c];
-            if (k0 + 512 < d) {
+            if (k0 + 512 < k_end) {
                 xv = *reinterpret_cast<const u32x4_t*>(xrow + k0 + 512);
 #pragma unroll
                 for (int c = 0; c < kWGroup; ++c)
@@ -552,14 +572,32 @@ __global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
                 }
             }
         }
+        if (WPT == 1) {
 #pragma unroll
-        for (int c = 0; c < kWGroup; ++c) {
-            if (c < ng) {
-                const double sc = wave_sum_f64(acc[c]);
-                if (lane == 0) csc[g0 + c] = sc;
+            for (int c = 0; c < kWGroup; ++c) {
+                if (c < ng) {
+                    const double sc = wave_sum_f64(acc[c]);
+                    if (lane == 0) csc[g0 + c] = sc;
+                }
             }
+        } else {
+            // the waves' shares meet in LDS and are added in wave order
+#pragma unroll
+            for (int c = 0; c < kWGroup; ++c) {
+                const double sc = wave_sum_f64(acc[c]);
+                if (lane == 0) s_share[sub][c] = sc;
+            }
+            __syncthreads();
+            if (sub == 0 && lane < ng) {
+                double sc = s_share[0][lane];
+#pragma unroll
+                for (int q = 1; q < WPT; ++q) sc += s_share[q][lane];
+                csc[g0 + lane] = sc;
+            }
+            __syncthreads();
         }
     }
+    if (WPT > 1 && sub != 0) return;                     // the token's first wave ranks
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_wave_barrier();
 
@@ -1065,13 +1103,24 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
                        a.part, a.xn2, a.gn2);
     if (a.T >= kWideSelectTokens) {
         // many tokens: one wave per token (throughput)
-        dim3 g2((a.T + kWTok - 1) / kWTok);
-        auto k = a.E <= 128 ? router_select_wave_kernel<2>
-                 : a.E <= 320 ? router_select_wave_kernel<5>
-                 : a.E <= 512 ? router_select_wave_kernel<8>
-                              : router_select_wave_kernel<kMaxExperts / 64>;
-        hipLaunchKernelGGL(k, g2, dim3(64 * kWTok), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
-                           a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+        if (a.T < kSplitSelectTokens) {
+            // few tokens for a wave each: every token's K chunks split over a workgroup
+            dim3 g2(a.T);
+            auto k = a.E <= 128 ? router_select_wave_kernel<2, kWTok>
+                     : a.E <= 320 ? router_select_wave_kernel<5, kWTok>
+                     : a.E <= 512 ? router_select_wave_kernel<8, kWTok>
+                                  : router_select_wave_kernel<kMaxExperts / 64, kWTok>;
+            hipLaunchKernelGGL(k, g2, dim3(64 * kWTok), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
+                               a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+        } else {
+            dim3 g2((a.T + kWTok - 1) / kWTok);
+            auto k = a.E <= 128 ? router_select_wave_kernel<2, 1>
+                     : a.E <= 320 ? router_select_wave_kernel<5, 1>
+                     : a.E <= 512 ? router_select_wave_kernel<8, 1>
+                                  : router_select_wave_kernel<kMaxExperts / 64, 1>;
+            hipLaunchKernelGGL(k, g2, dim3(64 * kWTok), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
+                               a.topk, a.offset, a.L, a.topk_ids, a.topk_w, a.local_ids);
+        }
     } else {
         // few tokens: a workgroup per token (latency)
         dim3 g2(a.T);

@@ -53,10 +53,10 @@ def test_widest_layers(wl, path, mode):
     assert err <= tol(mode)
 
 
-@pytest.mark.parametrize("T", [2, 3, 16, 40, 1100])
+@pytest.mark.parametrize("T", [2, 3, 16, 40, 600, 1100])
 def test_route_1024_experts_top32(T):
     """E = 1024, top-32: a workgroup per token for the selection (T = 2, 3, 16,
-    40), a wave per token (T = 1100)."""
+    40), four waves per token (T = 600), a wave per token (T = 1100)."""
     require_gpu()
     w = workloads.replace(MANY_E, T=T, d=256)
     log(f"route E=1024 k=32 T={T}")

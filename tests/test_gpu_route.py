@@ -76,17 +76,20 @@ def test_route_zero_tokens_tie_to_lowest_ids():
     _check(x, G, w, 0, w.E)
 
 
-def test_route_wide_select_zero_tokens_and_shard():
-    """T >= 512 takes the one-wave-per-token selection: zero tokens (every expert
-    a candidate) and a shard filter, against the oracle."""
+@pytest.mark.parametrize("T", [600, 1100])
+def test_route_wide_select_zero_tokens_and_shard(T):
+    """From 512 tokens the selection runs a wave per token (from 1024) or four
+    waves per token, each re-scoring a quarter of K (below): zero tokens (every
+    expert a candidate) and a shard filter, against the oracle."""
     require_gpu()
-    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=1100)
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     x = workloads.gen_hidden(w, "cuda")
-    for t in (0, 63, 64, 1099):
+    zeros = (0, 63, 64, T - 1)
+    for t in zeros:
         x[t] = 0
     G = workloads.gen_gate(w, "cuda")
     ids, wts, *_ = _route_gpu(x, G.t().contiguous(), w, 0, w.E, True)
-    for t in (0, 63, 64, 1099):
+    for t in zeros:
         assert ids[t].tolist() == list(range(w.k))
         assert np.allclose(wts[t], 1.0 / w.k, rtol=0, atol=1e-7)
     amb, diff, P = _check(x, G, w, 100, 150)
