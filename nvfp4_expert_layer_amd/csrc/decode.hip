@@ -64,7 +64,8 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     constexpr int ROWS = 4 * TGM;
     static_assert(FULLA || RGS == 1, "chunked A stages serve one row group");
     static_assert(!SEG || DEPTH % 4 == 0, "scale segments cover four steps");
-    const int tid = threadIdx.x, lane = tid & 63;
+    // (in a workgroup of several K groups of kDecWaves waves, a group's own threads)
+    const int tid = threadIdx.x & (64 * kDecWaves - 1), lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
     const int ntg = (ntok + 3) >> 2;
     const int nsteps = (K + 255) / 256;                      // K % 128 == 0
@@ -381,22 +382,31 @@ __device__ __forceinline__ bool dec_merge_tiles(const GemmArgs& a, DecTile& t, i
 // [c0 + 32 j, +16) and [c0 + 32 j + 16, +16), waves 2,3 the matching up rows (the
 // prefetch ring runs on across row groups); the up results meet the gate
 // results in LDS.  grid (max_tiles, F / (32 RG)).
+// KSPLIT > 1 (few experts touched, so few workgroups): the workgroup holds
+// KSPLIT groups of those four waves, group q streaming K slice q of d (its own
+// token-row stage); the groups' sums meet in LDS and are added in slice order.
+// A wave's stream, a chain of dependent ring rounds, is then KSPLIT times
+// shorter, with no synchronisation beyond the workgroup.
 // ---------------------------------------------------------------------------
-template <int MODE, int TGM, int DEPTH, bool FULLA, bool SEG, int RG>
-__global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
+template <int MODE, int TGM, int DEPTH, bool FULLA, bool SEG, int RG, int KSPLIT = 1>
+__global__ __launch_bounds__(64 * kDecWaves * KSPLIT) void dec_gemm1_kernel(GemmArgs a) {
     constexpr int ROWS = 4 * TGM;
+    static_assert(KSPLIT == 1 || FULLA, "K slices stage their whole slice");
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    __shared__ const uint16_t* s_arow[ROWS];
+    __shared__ const uint16_t* s_arow[KSPLIT][ROWS];
     // up results of row group j at [j & 1]: a gate wave reads group j before it
     // reaches the barrier of group j + 1, so group j + 2 can reuse the buffer
     __shared__ float s_up[2][2][TGM][64];
+    __shared__ float s_kred[KSPLIT > 1 ? KSPLIT - 1 : 1][kDecWaves][TGM][64];   // slices 1.. of the sums
     int tile, cb;
     dec_block<RG != 2>(tile, cb);
     if (tile >= *a.ntiles) return;
     const DecTile tl = dec_tile(a, tile);
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
     const int d = a.d, F = a.F;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & (64 * kDecWaves - 1), lane = tid & 63, wave = tid >> 6;
+    const int kq = threadIdx.x / (64 * kDecWaves);   // K slice of this wave's group
+    const int kk = d / KSPLIT, kb = kq * kk;
     const int half = wave & 1;                       // which 16 columns
     const bool is_up = wave >= 2;
     const int col0 = cb * (32 * RG) + half * 16;
@@ -407,26 +417,41 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
         const int row = tl.rb + tid;
         int t = 0;
         if (row < tl.re) t = tl.shared ? row - a.T * a.topk : a.perm[row] / a.topk;
-        s_arow[tid] = act_in + (size_t)t * d;
+        s_arow[kq][tid] = act_in + (size_t)t * d + kb;
     }
     __syncthreads();
     const uint8_t* w13 = W.w13 + tl.ex * (size_t)(2 * F) * (d / 2);
     const uint8_t* w13s = W.w13_s + tl.ex * (size_t)(2 * F) * (d / 16);
     const int wrow = (is_up ? F : 0) + col0 + n;
-    const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2)};
-    const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16)};
+    const uint8_t* const codes[1] = {w13 + (size_t)wrow * (d / 2) + kb / 2};
+    const uint8_t* const scales[1] = {w13s + (size_t)wrow * (d / 16) + kb / 16};
     const float g13 = W.g13[tl.ex] * a.a1g;          // weight global x activation global
     auto epi = [&](int j, const f32x4_t (&acc)[TGM][1]) {
         const int col = col0 + 32 * j + n;
         float v[TGM];
 #pragma unroll
-        for (int tg = 0; tg < TGM; ++tg) v[tg] = dec_result<TGM, 1>(acc, tg, 0, g) * g13;
-        if (is_up) {
+        for (int tg = 0; tg < TGM; ++tg) v[tg] = dec_result<TGM, 1>(acc, tg, 0, g);
+        if (KSPLIT > 1) {
+            if (kq > 0) {
+#pragma unroll
+                for (int tg = 0; tg < TGM; ++tg) s_kred[kq > 0 ? kq - 1 : 0][wave][tg][lane] = v[tg];
+            }
+            __syncthreads();
+            if (kq == 0) {
+#pragma unroll
+                for (int q = 1; q < KSPLIT; ++q)
+#pragma unroll
+                    for (int tg = 0; tg < TGM; ++tg) v[tg] += s_kred[q - 1][wave][tg][lane];
+            }
+        }
+#pragma unroll
+        for (int tg = 0; tg < TGM; ++tg) v[tg] *= g13;
+        if (is_up && kq == 0) {
 #pragma unroll
             for (int tg = 0; tg < TGM; ++tg) s_up[j & 1][half][tg][lane] = v[tg];
         }
         __syncthreads();
-        if (!is_up) {
+        if (!is_up && kq == 0) {
 #pragma unroll
             for (int tg = 0; tg < TGM; ++tg) {
                 const float gt = v[tg], up = s_up[j & 1][half][tg][lane];
@@ -446,7 +471,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_gemm1_kernel(GemmArgs a) {
         }
     };
     const size_t cstride = (size_t)32 * (d / 2), sstride = (size_t)32 * (d / 16);
-    dec_stream<1, TGM, DEPTH, RG, FULLA, SEG>(s_arow, ntok, d, codes, scales, cstride, sstride, lds, epi);
+    uint16_t* const stage = lds + (size_t)kq * (dec_lds_bytes(ROWS, kk, FULLA) / 2);
+    dec_stream<1, TGM, DEPTH, RG, FULLA, SEG>(s_arow[kq], ntok, kk, codes, scales, cstride, sstride, stage, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -953,13 +979,19 @@ int dec_rows(int T, int topk, int E) {
 
 // Launch of a decode kernel with `lds` bytes of dynamic LDS (above 64 KB the
 // kernel's limit is raised first; a failure is left for hipGetLastError).
-template <auto Kern>
+template <auto Kern, int GROUPS = 1>
 static void launch_dec(dim3 grid, int lds, hipStream_t s, const GemmArgs& a) {
     if (allow_dynamic_lds<Kern>(lds) != hipSuccess) return;
-    hipLaunchKernelGGL(Kern, grid, dim3(64 * kDecWaves), lds, s, a);
+    hipLaunchKernelGGL(Kern, grid, dim3(64 * kDecWaves * GROUPS), lds, s, a);
 }
 
 constexpr int kG1Depth = 4;         // prefetch ring depth of the small-tile GEMM1
+// GEMM1 in two K slices per workgroup up to this many expected workgroups.
+// Measured on the 4096 x 1024 layer with 160 local experts (GEMM1 stage time,
+// one slice / two / four): T = 1 (160 workgroups) 15.3 / 13.8 / 16.2 us; T = 2
+// (285) 19.2 / 19.5 / 26.3; T = 4 (525) 24.6 / 28.8 / 37.9; T = 8 40.1 / 44.6 /
+// 60.5.  Four slices (1024-thread workgroups) never paid.
+constexpr double kG1Split2Wgs = 200.0;
 
 // Expected number of expert tiles (touched local experts, plus the shared
 // expert) under uniform routing: L (1 - (1 - k/E)^T) + shared.
@@ -1011,9 +1043,27 @@ static void launch_g1_rg(const GemmArgs& a, hipStream_t s) {
     }
 }
 
+// K slices of GEMM1 within a workgroup (4-row tiles, one row group per wave):
+// when the grid's expected workgroups are few, KSPLIT groups of four waves share
+// each workgroup's columns, each streaming 1/KSPLIT of d.
+static int g1_kslices(const GemmArgs& a) {
+    if (dec_rows(a.T, a.topk, a.E) != 4 || g1_row_groups(a) != 1 || a.F % 32 != 0) return 1;
+    const double wgs = expected_tiles(a) * (a.F / 32);
+    if (wgs <= kG1Split2Wgs && a.d % 2048 == 0 && 2 * dec_lds_bytes(4, a.d / 2, true) <= kFullALds) return 2;
+    return 1;
+}
+
+template <int MODE, int KSPLIT>
+static void launch_g1_ksplit(const GemmArgs& a, hipStream_t s) {
+    const int lds = KSPLIT * dec_lds_bytes(4, a.d / KSPLIT, true);
+    launch_dec<dec_gemm1_kernel<MODE, 1, kG1Depth, true, true, 1, KSPLIT>, KSPLIT>(dim3(a.max_tiles, a.F / 32), lds,
+                                                                                   s, a);
+}
+
 hipError_t launch_dec_gemm1(const GemmArgs& a, hipStream_t s) {
     const int rows = dec_rows(a.T, a.topk, a.E);
-    if (rows == 4) a.mode == 0 ? launch_g1_rg<0, 1, kG1Depth>(a, s) : launch_g1_rg<1, 1, kG1Depth>(a, s);
+    if (g1_kslices(a) == 2) a.mode == 0 ? launch_g1_ksplit<0, 2>(a, s) : launch_g1_ksplit<1, 2>(a, s);
+    else if (rows == 4) a.mode == 0 ? launch_g1_rg<0, 1, kG1Depth>(a, s) : launch_g1_rg<1, 1, kG1Depth>(a, s);
     else if (rows == 8) a.mode == 0 ? launch_g1_rg<0, 2, kG1Depth>(a, s) : launch_g1_rg<1, 2, kG1Depth>(a, s);
     else a.mode == 0 ? launch_g1_rg<0, 4, 2>(a, s) : launch_g1_rg<1, 4, 2>(a, s);
     return hipGetLastError();

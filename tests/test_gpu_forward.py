@@ -241,6 +241,33 @@ def test_full_size_decode_other_token_counts(T):  # forced onto the block-diagon
     whole_output_check(lay, w.offset, w.L, w.has_shared, w.mode, f"decode T={T}", nv.PATH_DECODE)
 
 
+@pytest.mark.parametrize("mode", [W4A16, W4A4])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+def test_full_size_decode_small_batches(T, mode):
+    """The 320-expert shard at 1-16 tokens, where few experts are touched (at
+    T = 1 GEMM1's workgroups split d = 4096 into two K slices of 2048 between
+    two groups of four waves).  Whole output against the oracle, on a workspace
+    poisoned with 0xFF bytes, and bit-identical on a second call."""
+    require_gpu()
+    base = workloads.WORKLOADS["decode_shard0_w4a16"]
+    lay = full_layer("decode_shard0_w4a16")
+    w = workloads.replace(base, T=T, mode=mode, hidden_seed=base.hidden_seed + 1000 + T)
+    lay.w = w
+    lay.x = workloads.gen_hidden(w, "cuda")
+    log(f"full-size decode small batch T={T} mode={mode}")
+    p = nv.make_problem(T, w.d, w.F, w.E, w.k, w.offset, w.L, w.has_shared, mode)
+    assert nv.moe_nvfp4_resolved_path(p) == nv.PATH_DECODE
+    ws = nv.alloc_workspace(p)
+    ws.fill_(0xFF)
+    out = lay.run(w.offset, w.L, w.has_shared, mode, ws=ws)
+    again = lay.run(w.offset, w.L, w.has_shared, mode, ws=ws)
+    assert torch.equal(out, again)
+    ref = lay.oracle_full(w.offset, w.L, w.has_shared, mode)
+    err = rel_err(out, ref["out"])
+    log(f"  whole-output normwise rel err {err:.3e} (limit {tol(mode):g})")
+    assert err <= tol(mode)
+
+
 def test_full_size_two_shards_sum_to_unsharded_oracle():
     """Shard 0 (experts 0-159, with the shared expert) plus shard 1 (160-319) at
     the second shard's token count, W4A4: each shard's whole output against the
