@@ -38,7 +38,7 @@ def _graph_vs_eager(lay, offset, L, shared, mode, path, n_replays=3):
         gen.manual_seed(1000 + r)
         new_x = torch.randn(w.T, w.d, generator=gen, device="cuda").to(torch.bfloat16)
         if r == 1:
-            new_x[3] = 0                                   # a zero token in one replay
+            new_x[min(3, w.T - 1)] = 0                     # a zero token in one replay
         x.copy_(new_x)                                     # eager work between replays
         out.fill_(float("nan"))
         g.replay()
@@ -62,12 +62,14 @@ def test_graph_replays_match_eager_mid(mode, path):
     _graph_vs_eager(lay, 4, 16, True, mode, path)
 
 
-@pytest.mark.parametrize("T,path", [(64, nv.PATH_AUTO), (256, nv.PATH_DECODE), (384, nv.PATH_AUTO)])
+@pytest.mark.parametrize("T,path", [(1, nv.PATH_AUTO), (64, nv.PATH_AUTO), (256, nv.PATH_DECODE),
+                                    (384, nv.PATH_AUTO)])
 def test_graph_replays_match_eager_decode_shard(T, path):
-    """T = 64: exact routing, 4-row weight-streaming tiles; T = 256 (block-
-    diagonal path forced): certified routing, one-workgroup permutation, 8-row
-    tiles with more than 64 KB of LDS; T = 384: the dense weight-streaming path
-    AUTO picks there."""
+    """T = 1: selection and permutation in one workgroup, GEMM1 in two K slices
+    per workgroup; T = 64: exact routing, 4-row weight-streaming tiles; T = 256
+    (block-diagonal path forced): certified routing, one-workgroup permutation,
+    8-row tiles with more than 64 KB of LDS; T = 384: the dense weight-streaming
+    path AUTO picks there."""
     require_gpu()
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T)
     lay = Layer(w, experts_range=(0, w.L))
