@@ -2,6 +2,7 @@
 """Benchmark of the fused NVFP4 MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+                    [--workload NAME --tokens T]
 
 A step is one call of moe_nvfp4_forward (router top-k, shard filter,
 permutation, [W4A4 activation quantizer], GEMM1 + SwiGLU, GEMM2, weighted
@@ -23,6 +24,8 @@ headline workload (the T=64 expert-shard decode step), with:
              T=512 W4A4 second shard, T=8192 all-expert W4A4 prefill, T=16384
              Zipf-skewed W4A16 shard), each with its own roofline and oracle
 --all prints one line per workload instead (a report, not the default line).
+--tokens runs the named workload alone at another token count (e.g. the
+decode shard at T=1), with every measurement above; its traffic is null.
 """
 import argparse
 import re
@@ -56,6 +59,7 @@ CPU_SAMPLE = {"tiny_w4a16": 16, "decode_shard0_w4a16": 24, "shard1_w4a4_t512": 2
               "shard1_w4a4_static_t512": 24, "prefill_all_w4a4": 16, "prefill_zipf_shard0_w4a16": 32}
 STAGES = ["route_permute", "act_quant", "gemm1_swiglu", "gemm2", "combine"]
 G1_EVERY = 4                    # timed steps per GEMM1 event pair
+TOKENS_OVERRIDDEN = False       # --tokens: the workload runs at another token count
 PREWARM_S = 0.3                 # untimed forward calls before the warm-up steps (clock settling)
 CSRC = os.path.join(ROOT, "nvfp4_expert_layer_amd", "csrc")
 from nvfp4_expert_layer_amd.build import EXTRA_FLAGS as BUILD_FLAGS   # noqa: E402  (plain dict, no compilation)
@@ -91,7 +95,7 @@ def measured_traffic(path, workload):
     scaled by a plain copy's reading), or None when there is none or the kernel
     sources changed since the counters were taken."""
     fn = os.path.join(ROOT, "profiles", f"traffic_gemm1_{workload}.txt")
-    if not os.path.exists(fn):
+    if TOKENS_OVERRIDDEN or not os.path.exists(fn):      # (the counters are of the workload's own T)
         return None
     vals = {}
     with open(fn) as fh:
@@ -459,6 +463,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=list(workloads.WORKLOADS))
     ap.add_argument("--all", action="store_true", help="one line per workload")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="run --workload at this many tokens instead (its other sizes and seeds kept; "
+                         "no secondary workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -480,6 +487,14 @@ def main():
         print(json.dumps({"error": "this layer runs on one GPU: the expert shard is exercised by running one "
                                    "shard's experts locally; --gpus must be 1"}))
         sys.exit(2)
+    if args.tokens is not None:
+        if args.tokens < 1 or args.all:
+            print(json.dumps({"error": "--tokens needs a positive count and one --workload"}))
+            sys.exit(2)
+        global TOKENS_OVERRIDDEN
+        TOKENS_OVERRIDDEN = True
+        workloads.WORKLOADS[args.workload] = workloads.replace(workloads.WORKLOADS[args.workload], T=args.tokens)
+        args.no_secondary = True
     if args.all:
         names = list(workloads.WORKLOADS)
     else:
