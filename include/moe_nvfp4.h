@@ -130,7 +130,10 @@ typedef enum {
                                     workgroup per CU, grid barriers) for 1..16 tokens;
                                     needs d_model, d_ff <= 4096, d_model % 256 == 0, and
                                     the device otherwise idle for the launch's duration
-                                    (its barriers wait for every CU's workgroup)          */
+                                    (its barriers wait for every CU's workgroup).  The
+                                    waits are bounded: if one expires the kernel still
+                                    ends, but `out` is then undefined (the 32-bit word
+                                    at byte offset 4 of the workspace is then non-zero) */
 } moe_nvfp4_path;
 
 typedef struct {
