@@ -106,6 +106,11 @@ def _ptr(t):
         return None
     if not t.is_cuda:
         raise ValueError("tensor must be on the GPU")
+    # the library launches on the current device (and the stream): a tensor of
+    # another device would be read through pointers that device does not map
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"tensor is on {t.device}, the current device is cuda:{cur}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
@@ -134,6 +139,9 @@ def _rows(p):
 
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
+    cur = torch.cuda.current_device()
+    if s.device.index != cur:
+        raise ValueError(f"stream is on {s.device}, the current device is cuda:{cur}")
     return ctypes.c_void_p(s.cuda_stream)
 
 

@@ -105,3 +105,17 @@ def test_prepare_checks_checkpoint_and_destination():
     ck = nv.NVFP4Experts.empty(6, D, F, device="cpu")
     with pytest.raises(ValueError, match="must be on the GPU"):
         nv.moe_nvfp4_prepare(ck, 0, 0, 1, 2, dst)
+
+
+def test_tensors_and_stream_of_another_device_are_refused(monkeypatch):
+    """The library launches on the current device: a tensor or a stream of
+    another device is refused before any pointer reaches it."""
+    from types import SimpleNamespace
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    other = SimpleNamespace(is_cuda=True, device=torch.device("cuda", 1), is_contiguous=lambda: True,
+                            data_ptr=lambda: 0)
+    with pytest.raises(ValueError, match="current device is cuda:0"):
+        nv._ptr(other)
+    stream = SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0)
+    with pytest.raises(ValueError, match="current device is cuda:0"):
+        nv._stream(stream)
