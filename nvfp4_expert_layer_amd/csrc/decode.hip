@@ -118,36 +118,20 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     };
     // SEG: scales come in 16-byte segments, one per step (the four lane groups'
     // chunks); lane group m loads the segment of step 4G + m of group G (64
-    // adjacent bytes per row), and a 4x4 transpose across lane groups (two
-    // permlane32 and two permlane16 swaps) leaves in lane group g, register m,
-    // the 4 scale bytes of its own chunk at step 4G + m.  Needs K % 1024 == 0.
+    // adjacent bytes per row), and scale_seg_transpose leaves in lane group g,
+    // register m, the 4 scale bytes of its own chunk at step 4G + m.  Needs
+    // K % 1024 == 0.
     auto load_seg = [&](int r, int grp) -> u32x4_t {
         int v = grp * 4 + g;
         v = v < nvirt ? v : nvirt - 1;
         const int j = v / nsteps, step = v - j * nsteps;
         return *reinterpret_cast<const u32x4_t*>(scales[r] + j * sstride + (size_t)step * 16);
     };
-    auto transpose4 = [](u32x4_t x) -> u32x4_t {
-        unsigned r0 = x.x, r1 = x.y, r2 = x.z, r3 = x.w;
-        auto p = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
-        r0 = p[0];
-        r2 = p[1];
-        p = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
-        r1 = p[0];
-        r3 = p[1];
-        p = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
-        r0 = p[0];
-        r1 = p[1];
-        p = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
-        r2 = p[0];
-        r3 = p[1];
-        return u32x4_t{r0, r1, r2, r3};
-    };
     u32x4_t seg_next[NR], seg_cur[NR];
     if (SEG) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            seg_cur[r] = transpose4(load_seg(r, 0));
+            seg_cur[r] = scale_seg_transpose(load_seg(r, 0));
             seg_next[r] = load_seg(r, 1);
         }
     }
@@ -208,7 +192,7 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
             // next group of four steps: its segment arrived long ago; fetch the one after
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
-                seg_cur[r] = transpose4(seg_next[r]);
+                seg_cur[r] = scale_seg_transpose(seg_next[r]);
                 seg_next[r] = load_seg(r, v / 4 + 1);
             }
         }

@@ -67,6 +67,36 @@ __device__ __forceinline__ f16x2_t e4m3x2_hi_to_f16(uint32_t quad) {
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(quad, 1.0f, true);
 }
 
+// Block scales of a weight-streaming step in 16-byte segments.  A step covers
+// 256 elements of K: lane group g (lanes 16 g .. 16 g + 15) takes the 64-element
+// chunk 4 s + g of its row, whose four E4M3 scales are dword g of the row's
+// 16-byte scale segment of step s.  Lane group m loads the whole segment of step
+// 4 G + m (one 16-byte load per four steps instead of a 4-byte load per step);
+// this 4 x 4 transpose across the lane groups (two permlane32 and two permlane16
+// swaps) then leaves in lane group g, dword m, the scales of its own chunk at
+// step 4 G + m.
+__device__ __forceinline__ u32x4_t scale_seg_transpose(u32x4_t x) {
+    unsigned r0 = x.x, r1 = x.y, r2 = x.z, r3 = x.w;
+    auto p = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+    r0 = p[0];
+    r2 = p[1];
+    p = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+    r1 = p[0];
+    r3 = p[1];
+    p = __builtin_amdgcn_permlane16_swap(r0, r1, false, false);
+    r0 = p[0];
+    r1 = p[1];
+    p = __builtin_amdgcn_permlane16_swap(r2, r3, false, false);
+    r2 = p[0];
+    r3 = p[1];
+    return u32x4_t{r0, r1, r2, r3};
+}
+
+// Dword i (0..3, runtime) of a segment.
+__device__ __forceinline__ uint32_t seg_word(const u32x4_t& x, int i) {
+    return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
+}
+
 // Two E2M1 codes (byte `sel` of `src`) -> exact fp32 values.
 template <int SEL>
 __device__ __forceinline__ f32x2_t fp4x2_to_f32(uint32_t src) {
