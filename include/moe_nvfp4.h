@@ -112,7 +112,7 @@ typedef enum {
  * expert, T * top_k / num_experts (the shard's expected load, not the global
  * one), with crossovers measured on the 4096 x 1024 layer:
  *   W4A16 with d_model % 256 == 0: block-diagonal weight streaming (DECODE) up
- *     to 4.6, dense weight streaming (MID) up to 44, tiles (PREFILL) above;
+ *     to 3.9, dense weight streaming (MID) up to 64, tiles (PREFILL) above;
  *   W4A4 with d_model and d_ff multiples of 256, at most 8192 (the activations
  *     then travel as NVFP4): DECODE up to 5, MID up to 18, PREFILL above;
  *   W4A4 with d_model and d_ff multiples of 256 above 8192: DECODE up to 6,

@@ -56,10 +56,10 @@ int resolve_path(const moe_nvfp4_problem& p) {
     // expected local pairs per local expert: T * k / E (uniform routing).  The
     // crossovers were measured on the 4096 x 1024 layer with 160 local experts
     // (per-call medians, us):
-    //   W4A16: block-diagonal weight streaming up to ~4.6 pairs per expert
-    //   (T = 176: 328 against 337 dense; T = 192: 346 against 340), the dense
-    //   weight-streaming kernels up to ~44 (T = 1536: 671 against 709 tiled;
-    //   T = 2048: 774 against 754), then the tiles;
+    //   W4A16: block-diagonal weight streaming up to ~3.9 pairs per expert
+    //   (T = 152: 303 against 307 dense; T = 160: 318 against 308), the dense
+    //   weight-streaming kernels up to ~64 (T = 2304: 746 against 809 tiled;
+    //   T = 2560: 811 against 811; T = 2816: 893 against 829), then the tiles;
     //   W4A4 with the activations as NVFP4: block-diagonal up to 5 (T = 192:
     //   311 against 313 dense; T = 224: 357 against 315), dense up to 18
     //   (T = 704: 368 against 388 tiled; T = 768: 403 against 391), tiles above;
@@ -68,8 +68,8 @@ int resolve_path(const moe_nvfp4_problem& p) {
     const double per_expert = (double)p.num_tokens * p.top_k / p.num_experts;
     const bool w4a4 = is_w4a4(p.mode);
     if (!w4a4 && moe::mid_ok(p.d_model, p.d_ff)) {
-        if (per_expert <= 4.6) return MOE_NVFP4_PATH_DECODE;
-        return per_expert <= 44.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
+        if (per_expert <= 3.9) return MOE_NVFP4_PATH_DECODE;
+        return per_expert <= 64.0 ? MOE_NVFP4_PATH_MID : MOE_NVFP4_PATH_PREFILL;
     }
     if (w4a4 && moe::mid_packed_ok(p.d_model, p.d_ff)) {
         if (per_expert <= 5.0) return MOE_NVFP4_PATH_DECODE;

@@ -92,17 +92,17 @@ def test_workspace_grows_with_tokens_and_empty_batch_is_valid():
 
 def test_resolved_path_crossover():
     # expected local pairs per local expert T*k/E: W4A16 streams with the
-    # block-diagonal kernels up to 4.6, with the dense ones up to 44 (d % 256
+    # block-diagonal kernels up to 3.9, with the dense ones up to 64 (d % 256
     # == 0), then tiles; W4A4 with NVFP4 activations (d, F multiples of 256, at
     # most 8192) up to 5 and 18; larger packed W4A4 streams up to 6; W4A4 whose
     # d or F is not a multiple of 256 streams up to 9
     def path(T, mode, d=4096, F=1024, force=nv.PATH_AUTO):
         return nv.moe_nvfp4_resolved_path(nv.make_problem(T, d, F, 320, 8, 0, 160, True, mode, force))
     assert path(64, nv.W4A16) == nv.PATH_DECODE
-    assert path(184, nv.W4A16) == nv.PATH_DECODE          # 4.6
-    assert path(185, nv.W4A16) == nv.PATH_MID
-    assert path(1760, nv.W4A16) == nv.PATH_MID            # 44.0
-    assert path(1761, nv.W4A16) == nv.PATH_PREFILL
+    assert path(156, nv.W4A16) == nv.PATH_DECODE          # 3.9
+    assert path(157, nv.W4A16) == nv.PATH_MID
+    assert path(2560, nv.W4A16) == nv.PATH_MID            # 64.0
+    assert path(2561, nv.W4A16) == nv.PATH_PREFILL
     assert path(360, nv.W4A16, d=3968) == nv.PATH_DECODE  # d % 256 != 0: no dense path, threshold 9
     assert path(361, nv.W4A16, d=3968) == nv.PATH_PREFILL
     assert path(200, nv.W4A4) == nv.PATH_DECODE           # 5.0
