@@ -18,7 +18,8 @@ headline workload (the T=64 expert-shard decode step), with:
              weight streaming, the 16-bit MFMA peak for tiles): algorithmic
              bytes (or flops) per launch / its average duration from HIP events
              recorded around it in the timed steps, on the kernels' stream
-  graph_replay  the same forward captured once in a HIP graph, K replays timed
+  graph_replay  the same forward captured once in a HIP graph, pre-warmed
+             like the direct calls, K replays timed
   cpu_baseline  the CPU oracle timed on a bounded sample of the workload
   secondary  the same measurements for the other four workloads (tiny layer,
              T=512 W4A4 second shard, T=8192 all-expert W4A4 prefill, T=16384
@@ -128,9 +129,10 @@ GRAPH_PROBE_CALLS = 50
 
 
 def graph_probe(name):
-    """GRAPH_PROBE_CALLS direct forward calls, then the same forward captured in
-    a HIP graph and replayed 5 + GRAPH_PROBE_CALLS times, for a kernel trace
-    that compares the two (see --trace-summary).  Prints both wall times."""
+    """The forward captured in a HIP graph and replayed untimed for PREWARM_S,
+    then GRAPH_PROBE_CALLS direct forward calls and GRAPH_PROBE_CALLS replays,
+    for a kernel trace that compares the two (see --trace-summary).  Prints
+    both wall times."""
     w = workloads.WORKLOADS[name]
     local, shared = build_weights(w)
     gate_w = workloads.gen_gate(w, "cuda").t().contiguous()
@@ -139,17 +141,17 @@ def graph_probe(name):
     ws = nv.alloc_workspace(p)
     out = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
     prewarm(lambda: nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+    # the capture leaves the chip idle for a while: pre-warm again (with
+    # replays) so that both timed phases start at a settled clock
+    prewarm(graph.replay)
     t0 = time.perf_counter()
     for _ in range(GRAPH_PROBE_CALLS):
         nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
     torch.cuda.synchronize()
     direct = (time.perf_counter() - t0) / GRAPH_PROBE_CALLS
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
-    for _ in range(5):
-        graph.replay()
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(GRAPH_PROBE_CALLS):
         graph.replay()
@@ -163,13 +165,13 @@ def trace_summary(csv_path, per_call):
     """Per-kernel average durations and the mean gap between kernels in the two
     phases of a --graph-probe run, from rocprofv3's kernel_trace.csv: the last
     GRAPH_PROBE_CALLS forwards are graph replays, the GRAPH_PROBE_CALLS before
-    the 5 unmeasured replays are direct calls (per_call kernels a forward)."""
+    them direct calls (per_call kernels a forward)."""
     import csv
     import collections
     rows = [r for r in csv.DictReader(open(csv_path)) if "moe::" in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     n, c = len(rows), per_call * GRAPH_PROBE_CALLS
-    phases = {"direct": rows[n - 2 * c - 5 * per_call: n - c - 5 * per_call], "graph_replay": rows[n - c:]}
+    phases = {"direct": rows[n - 2 * c: n - c], "graph_replay": rows[n - c:]}
     for label, ph in phases.items():
         d = collections.OrderedDict()
         for r in ph:
@@ -309,6 +311,10 @@ def bench_workload(name, steps, warmup, hip):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         nv.moe_nvfp4_forward(p, x, gate_w, local, shared, ws, out)
+    # the capture leaves the chip idle long enough for its clock to drop:
+    # replays are pre-warmed like the direct calls (20 replays right after the
+    # capture measured 243 us per forward at T=64, 222 after 0.3 s of replays)
+    prewarm(graph.replay)
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
