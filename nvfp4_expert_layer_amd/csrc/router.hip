@@ -747,11 +747,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
 
 // All three permutation steps in one workgroup of 1024 threads, for T <= 512:
 // a bitmask of ceil(T/32) words per local expert (masks, [L][W]) marks the
-// tokens that chose it; a pair's rank is the popcount of the lower bits.
-// (Measured on the 320-expert shard: one launch instead of three saves 8 us at
-// T = 300 and 2.5 us at T = 512, and costs 23 us at T = 1024.)
+// tokens that chose it, and an exclusive prefix of its words' popcounts (pre,
+// 16-bit, [L][W]) makes a pair's rank within its expert two LDS reads: the
+// prefix of the token's word plus the popcount of the lower bits in it.
+// (Measured on the 320-expert
+// shard: one launch instead of three saves 8 us at T = 300 and 2.5 us at
+// T = 512, and costs 23 us at T = 1024.)
 constexpr int kPermSmallTokens = 512;
-constexpr int kPermSmallLds = 49152;        // bytes of bitmask
+constexpr int kPermSmallLds = 57344;        // bytes of bitmask + prefix (dynamic; the static arrays take the rest of 64 KB)
+
+__host__ __device__ constexpr size_t perm_small_lds(int T, int L) {
+    return (size_t)L * ((T + 31) / 32) * 6;
+}
 
 __device__ void perm_small_body(const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared,
                                 int BM, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -759,32 +766,62 @@ __device__ void perm_small_body(const int32_t* __restrict__ local_ids, int T, in
                                 int32_t* __restrict__ perm, int32_t* __restrict__ inv, uint32_t* masks) {
     __shared__ int32_t s_off[1024];
     const int W = (T + 31) >> 5;
+    uint16_t* const pre = reinterpret_cast<uint16_t*>(masks + L * W);
     const int tid = threadIdx.x;
+    const bool tok = tid < T;
+    const int wd = tid >> 5;
+    const uint32_t bit = 1u << (tid & 31);
+    const size_t row = (size_t)(tok ? tid : 0) * topk;
+    // the token's first eight ids, loaded by the waves that hold tokens (a
+    // wave-uniform branch; within it a clamped index re-reads the last id, and
+    // only the uses are conditional)
+    int lj[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    if (topk > 0 && __builtin_amdgcn_readfirstlane(tid) < T) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) lj[q] = local_ids[row + min(q, topk - 1)];
+    }
     for (int i = tid; i < L * W; i += 1024) masks[i] = 0u;
     __syncthreads();
-    if (tid < T)
-        for (int j = 0; j < topk; ++j) {
-            const int lam = local_ids[(size_t)tid * topk + j];
-            if ((unsigned)lam < (unsigned)L) atomicOr(&masks[lam * W + (tid >> 5)], 1u << (tid & 31));
+    if (tok) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (q < topk && (unsigned)lj[q] < (unsigned)L) atomicOr(&masks[lj[q] * W + wd], bit);
+        for (int j = 8; j < topk; ++j) {
+            const int lam = local_ids[row + j];
+            if ((unsigned)lam < (unsigned)L) atomicOr(&masks[lam * W + wd], bit);
         }
+    }
     __syncthreads();
     int c = 0;
     if (tid < L)
-        for (int w = 0; w < W; ++w) c += __popc(masks[tid * W + w]);
+        for (int w = 0; w < W; ++w) {
+            pre[tid * W + w] = (uint16_t)c;
+            c += __popc(masks[tid * W + w]);
+        }
     scan_and_emit_tiles(c, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, s_off);
     __syncthreads();
-    for (int p = tid; p < T * topk; p += 1024) {
-        const int t = p / topk;
-        const int lam = local_ids[p];
-        int pos = -1;
-        if ((unsigned)lam < (unsigned)L) {
-            int r = 0;
-            for (int w = 0; w < (t >> 5); ++w) r += __popc(masks[lam * W + w]);
-            r += __popc(masks[lam * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
-            pos = s_off[lam] + r;
-            perm[pos] = p;
+    // one thread per pair (up to four each, their ids loaded together; a wave
+    // whose first pair is past the end loads nothing)
+    const int np = T * topk;
+    for (int p0 = 0; p0 < np; p0 += 4096) {
+        int lp[4] = {-1, -1, -1, -1};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (__builtin_amdgcn_readfirstlane(p0 + u * 1024 + tid) < np)
+                lp[u] = local_ids[min(p0 + u * 1024 + tid, np - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = p0 + u * 1024 + tid;
+            if (p >= np) break;
+            const int t = p / topk, lam = lp[u];
+            int pos = -1;
+            if ((unsigned)lam < (unsigned)L) {
+                const int w = t >> 5;
+                pos = s_off[lam] + pre[lam * W + w] + __popc(masks[lam * W + w] & ((1u << (t & 31)) - 1u));
+                perm[pos] = p;
+            }
+            inv[p] = pos;
         }
-        inv[p] = pos;
     }
 }
 
@@ -792,7 +829,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
     const int32_t* __restrict__ local_ids, int T, int topk, int L, int has_shared, int BM,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int4* __restrict__ tiles,
     int32_t* __restrict__ ntiles, int max_tiles, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-    extern __shared__ uint32_t masks[];                    // [L][ceil(T/32)]
+    extern __shared__ uint32_t masks[];                    // [L][ceil(T/32)] words, then the 16-bit prefix
     perm_small_body(local_ids, T, topk, L, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, perm, inv,
                     masks);
 }
@@ -988,7 +1025,7 @@ template <int EPL>
 __global__ __launch_bounds__(1024) void router_exact_finish_kernel(RouterArgs r, PermArgs q) {
     extern __shared__ __attribute__((aligned(16))) unsigned char fl[];
     double* const s_val = reinterpret_cast<double*>(fl);                              // [T][E]
-    uint32_t* const masks = reinterpret_cast<uint32_t*>(fl + (size_t)r.T * r.E * 8);   // [L][ceil(T/32)]
+    uint32_t* const masks = reinterpret_cast<uint32_t*>(fl + (size_t)r.T * r.E * 8);   // [L][ceil(T/32)] + prefix
     __shared__ int32_t s_id[kFuseTokens][32];
     __shared__ double s_sc[kFuseTokens][32];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1182,7 +1219,7 @@ hipError_t launch_route_exact(const RouterArgs& a, hipStream_t s) {
 }
 
 static size_t route_fused_lds(int T, int E, int L) {
-    return (size_t)T * E * 8 + (size_t)L * ((T + 31) / 32) * 4;
+    return (size_t)T * E * 8 + perm_small_lds(T, L);
 }
 
 bool route_fused_ok(int T, int E, int d, int L) {
@@ -1207,7 +1244,7 @@ hipError_t launch_route_exact_fused(const RouterArgs& a, const PermArgs& q, hipS
 hipError_t launch_permute(const PermArgs& a, hipStream_t s) {
     const int nblk = (a.T + kPermBlock - 1) / kPermBlock;
     const size_t lds = (size_t)a.L * (kPermBlock / 32) * sizeof(uint32_t);
-    const size_t small_lds = (size_t)a.L * ((a.T + 31) / 32) * sizeof(uint32_t);
+    const size_t small_lds = perm_small_lds(a.T, a.L);
     if (a.T <= kPermSmallTokens && small_lds <= (size_t)kPermSmallLds) {
         // one workgroup (one launch) when the bitmask fits
         hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), small_lds, s, a.local_ids, a.T, a.topk, a.L,
