@@ -745,15 +745,15 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
     scan_and_emit_tiles(total, L, T, topk, has_shared, BM, counts, offsets, tiles, ntiles, max_tiles, nullptr);
 }
 
-// All three permutation steps in one workgroup of 1024 threads, for T <= 512:
+// All three permutation steps in one workgroup of 1024 threads, for T <= 1024:
 // a bitmask of ceil(T/32) words per local expert (masks, [L][W]) marks the
 // tokens that chose it, and an exclusive prefix of its words' popcounts (pre,
 // 16-bit, [L][W]) makes a pair's rank within its expert two LDS reads: the
 // prefix of the token's word plus the popcount of the lower bits in it.
-// (Measured on the 320-expert
-// shard: one launch instead of three saves 8 us at T = 300 and 2.5 us at
-// T = 512, and costs 23 us at T = 1024.)
-constexpr int kPermSmallTokens = 512;
+// Kernel time against the three-launch path on the 160-expert shard: T = 640
+// 7.9 us against 7.5 + 4.6 + 4.7, T = 1024 13.3 against 7.6 + 4.6 + 4.6 (plus
+// two launch gaps).
+constexpr int kPermSmallTokens = 1024;
 constexpr int kPermSmallLds = 57344;        // bytes of bitmask + prefix (dynamic; the static arrays take the rest of 64 KB)
 
 __host__ __device__ constexpr size_t perm_small_lds(int T, int L) {

@@ -143,11 +143,13 @@ def test_route_few_tokens_both_sides_of_the_exact_fp64_path(T):
         assert np.allclose(wts[1], 1.0 / w.k, rtol=0, atol=1e-7)
 
 
-@pytest.mark.parametrize("T,L", [(256, 160), (257, 160), (512, 160), (513, 160), (384, 1024), (385, 1024)])
+@pytest.mark.parametrize("T,L", [(256, 160), (512, 160), (1024, 160), (1025, 160), (288, 1024), (289, 1024)])
 def test_route_permutation_one_workgroup_and_blocked(T, L):
-    """Up to 512 tokens (bitmask of L x ceil(T/32) words within 48 KB) one
-    workgroup builds the whole permutation; beyond, per-256-token blocks, a scan
-    and a scatter.  Both sides of each bound, against the oracle."""
+    """Up to 1024 tokens (a bitmask of L x ceil(T/32) words and its 16-bit
+    prefix within 56 KB) one workgroup builds the whole permutation; beyond,
+    per-256-token blocks, a scan and a scatter.  Both sides of each bound
+    (the token bound at L = 160, the LDS bound at L = 1024), against the
+    oracle."""
     require_gpu()
     E = max(320, L)
     w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T, E=E, L=L, offset=0)
