@@ -53,14 +53,21 @@ __host__ __device__ constexpr int dec_lds_bytes(int rows, int K, bool full) {
 //   cstride / sstride: bytes to the same lane's row in the next sequential row group;
 //   arows: the tile's token rows (bf16, K long), ntok of them valid;
 //   epi(j, acc): called after sequential row group j with, per token group, the
-//   four tokens' sums over this lane group's K share.
+//   four tokens' sums over this lane group's K share;
+//   setup(): called once the weight ring's first loads are out and before the
+//   token rows are staged (it fills arows and synchronises the workgroup), so
+//   that its own memory round trips overlap the ring's.
 // A step covers 256 elements of K: lane group g takes the 64-element chunk
 // 4 i + g; chunks past K (K % 256 == 128) are skipped by the upper lane groups.
-template <int NR, int TGM, int DEPTH, int RGS, bool FULLA, bool SEG, class Epi>
+struct NoSetup {
+    __device__ void operator()() const {}
+};
+
+template <int NR, int TGM, int DEPTH, int RGS, bool FULLA, bool SEG, class Epi, class Setup = NoSetup>
 __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ arows, int ntok, int K,
                                            const uint8_t* const (&codes)[NR],
                                            const uint8_t* const (&scales)[NR], size_t cstride,
-                                           size_t sstride, uint16_t* lds, Epi epi) {
+                                           size_t sstride, uint16_t* lds, Epi epi, Setup setup = Setup{}) {
     constexpr int ROWS = 4 * TGM;
     static_assert(FULLA || RGS == 1, "chunked A stages serve one row group");
     static_assert(!SEG || DEPTH % 4 == 0, "scale segments cover four steps");
@@ -127,11 +134,13 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
         const int j = v / nsteps, step = v - j * nsteps;
         return *reinterpret_cast<const u32x4_t*>(scales[r] + j * sstride + (size_t)step * 16);
     };
+    // (the first segment is transposed once the token rows are staged, so
+    // that nothing before the stage waits for it)
     u32x4_t seg_next[NR], seg_cur[NR];
     if (SEG) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            seg_cur[r] = scale_seg_transpose(load_seg(r, 0));
+            seg_cur[r] = load_seg(r, 0);
             seg_next[r] = load_seg(r, 1);
         }
     }
@@ -142,6 +151,7 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     for (int u = 0; u < DEPTH; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) load_codes(r, u, wl[u][r], wh[u][r], ws[u][r]);
+    setup();
 
     if (FULLA) {
         // the whole K in batches of kABatch chunks: a batch's loads go out
@@ -161,6 +171,10 @@ __device__ __forceinline__ void dec_stream(const uint16_t* const* __restrict__ a
     } else {
         a_load(0);
         a_store(0, buf0);
+    }
+    if (SEG) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) seg_cur[r] = scale_seg_transpose(seg_cur[r]);
     }
 
     f32x4_t acc[TGM][NR];
@@ -340,6 +354,21 @@ __device__ __forceinline__ DecTile dec_tile(const GemmArgs& a, int tile) {
     return t;
 }
 
+// The tile entry and the live-tile count, loaded together (the grid's first
+// dimension is the table's capacity, so the entry is always inside the table);
+// false for a workgroup past the count.
+__device__ __forceinline__ bool dec_tile_live(const GemmArgs& a, int tile, DecTile& t) {
+    const int4 e = a.tiles[tile];
+    const int nt = *a.ntiles;
+    asm volatile("" ::: "memory");                   // both loads go out before the count is tested
+    if (tile >= nt) return false;
+    t.rb = e.y;
+    t.re = e.z;
+    t.shared = e.x == a.L;
+    t.ex = t.shared ? 0 : (size_t)e.x;
+    return true;
+}
+
 // MERGE consecutive table tiles of one group as one workgroup's rows: the tile
 // whose index within its group is a multiple of MERGE takes the rows of the
 // next MERGE - 1 tiles of the same group too; the others return (false).
@@ -384,8 +413,8 @@ __global__ __launch_bounds__(64 * kDecWaves * KSPLIT) void dec_gemm1_kernel(Gemm
     __shared__ float s_kred[KSPLIT > 1 ? KSPLIT - 1 : 1][kDecWaves][TGM][64];   // slices 1.. of the sums
     int tile, cb;
     dec_block<RG != 2>(tile, cb);
-    if (tile >= *a.ntiles) return;
-    const DecTile tl = dec_tile(a, tile);
+    DecTile tl;
+    if (!dec_tile_live(a, tile, tl)) return;
     const ExpertWeights& W = tl.shared ? a.shared : a.local;
     const int d = a.d, F = a.F;
     const int tid = threadIdx.x & (64 * kDecWaves - 1), lane = tid & 63, wave = tid >> 6;
@@ -397,13 +426,20 @@ __global__ __launch_bounds__(64 * kDecWaves * KSPLIT) void dec_gemm1_kernel(Gemm
     const int n = lane & 15, g = lane >> 4;
     const int ntok = tl.re - tl.rb;
     const uint16_t* act_in = MODE == 0 ? a.hidden : a.hq;
-    if (tid < ROWS) {
-        const int row = tl.rb + tid;
-        int t = 0;
-        if (row < tl.re) t = tl.shared ? row - a.T * a.topk : a.perm[row] / a.topk;
-        s_arow[kq][tid] = act_in + (size_t)t * d + kb;
-    }
-    __syncthreads();
+    // the pair of tile row tid % ROWS (the tile's last row past its end; any
+    // valid entry for the shared expert's rows, which need none), loaded by
+    // every thread before the weight ring goes out and used after it (setup)
+    const int pv = a.perm[min(min(tl.rb + (tid % ROWS), tl.re - 1), a.T * a.topk - 1)];
+    asm volatile("" ::: "memory");                   // issued here, not sunk to its use
+    auto setup = [&]() {
+        if (tid < ROWS) {
+            const int row = tl.rb + tid;
+            int t = 0;
+            if (row < tl.re) t = tl.shared ? row - a.T * a.topk : pv / a.topk;
+            s_arow[kq][tid] = act_in + (size_t)t * d + kb;
+        }
+        __syncthreads();
+    };
     const uint8_t* w13 = W.w13 + tl.ex * (size_t)(2 * F) * (d / 2);
     const uint8_t* w13s = W.w13_s + tl.ex * (size_t)(2 * F) * (d / 16);
     const int wrow = (is_up ? F : 0) + col0 + n;
@@ -456,7 +492,8 @@ __global__ __launch_bounds__(64 * kDecWaves * KSPLIT) void dec_gemm1_kernel(Gemm
     };
     const size_t cstride = (size_t)32 * (d / 2), sstride = (size_t)32 * (d / 16);
     uint16_t* const stage = lds + (size_t)kq * (dec_lds_bytes(ROWS, kk, FULLA) / 2);
-    dec_stream<1, TGM, DEPTH, RG, FULLA, SEG>(s_arow[kq], ntok, kk, codes, scales, cstride, sstride, stage, epi);
+    dec_stream<1, TGM, DEPTH, RG, FULLA, SEG>(s_arow[kq], ntok, kk, codes, scales, cstride, sstride, stage, epi,
+                                              setup);
 }
 
 // ---------------------------------------------------------------------------
