@@ -954,10 +954,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void micro_layer_kernel(MicroArgs a
             }
         }
         u32x4_t o;
-        o.x = f32_to_bf16_rne(sacc[0]) | (f32_to_bf16_rne(sacc[1]) << 16);
-        o.y = f32_to_bf16_rne(sacc[2]) | (f32_to_bf16_rne(sacc[3]) << 16);
-        o.z = f32_to_bf16_rne(sacc[4]) | (f32_to_bf16_rne(sacc[5]) << 16);
-        o.w = f32_to_bf16_rne(sacc[6]) | (f32_to_bf16_rne(sacc[7]) << 16);
+        o.x = f32x2_to_bf16x2(sacc[0], sacc[1]);
+        o.y = f32x2_to_bf16x2(sacc[2], sacc[3]);
+        o.z = f32x2_to_bf16x2(sacc[4], sacc[5]);
+        o.w = f32x2_to_bf16x2(sacc[6], sacc[7]);
         *reinterpret_cast<u32x4_t*>(a.out + (size_t)t * d + c0) = o;
     }
 }

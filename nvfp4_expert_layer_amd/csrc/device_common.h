@@ -40,11 +40,18 @@ constexpr int kBlock = 16;          // NVFP4 elements per block scale
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+// fp32 -> bf16 bits, round to nearest even: the hardware conversion
+// (v_cvt_pk_bf16_f32), one instruction where the integer rounding took four.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> bf16x2 bits {lo, hi}, round to nearest even, one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t){lo, hi}, bf16x2v_t));
 }
 
 // Upper halves of two fp32 values packed as bf16x2 (exact when both values are

@@ -58,10 +58,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         }
     }
     u32x4_t o;
-    o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
-    o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
-    o.z = f32_to_bf16_rne(s[4]) | (f32_to_bf16_rne(s[5]) << 16);
-    o.w = f32_to_bf16_rne(s[6]) | (f32_to_bf16_rne(s[7]) << 16);
+    o.x = f32x2_to_bf16x2(s[0], s[1]);
+    o.y = f32x2_to_bf16x2(s[2], s[3]);
+    o.z = f32x2_to_bf16x2(s[4], s[5]);
+    o.w = f32x2_to_bf16x2(s[6], s[7]);
     *reinterpret_cast<u32x4_t*>(a.out + (size_t)t * a.d + c0) = o;
 }
 

@@ -331,7 +331,7 @@ __global__ __launch_bounds__(64 * kPWaves) void pf_gemm_kernel(GemmArgs a) {
                 for (int e = 0; e < 8; ++e) o[e] = f32_to_f16_bits(x[2 * e]) | (f32_to_f16_bits(x[2 * e + 1]) << 16);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
+                for (int e = 0; e < 8; ++e) o[e] = f32x2_to_bf16x2(x[2 * e], x[2 * e + 1]);
             }
             uint16_t* dst = a.act + (size_t)(rb + row) * F + nt * 128 + cb;
             *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{o[0], o[1], o[2], o[3]};
