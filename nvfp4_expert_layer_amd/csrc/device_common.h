@@ -185,27 +185,18 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// fp32 -> E2M1 code (4 bits), zero magnitude -> +0.
+// fp32 -> E2M1 code (4 bits), zero magnitude -> +0.  The magnitude index is
+// the number of midpoints between {0, .5, 1, 1.5, 2, 3, 4, 6} (.25 .75 1.25
+// 1.75 2.5 3.5 5) that |r| passes; at a midpoint the even code wins, so the
+// comparison is strict where the upper neighbour is odd (.5, 1.5, 3, 6) and
+// inclusive where it is even (1, 2, 4).  Branch-free: seven compares and adds
+// instead of a chain of divergent branches.  Above 5, and for NaN, the index
+// is 7 (magnitude 6).
 __device__ __forceinline__ uint32_t e2m1_encode(float r) {
-    float a = fabsf(r);
-    uint32_t m;
-    // midpoints between {0, .5, 1, 1.5, 2, 3, 4, 6}: .25 .75 1.25 1.75 2.5 3.5 5;
-    // at a midpoint choose the even code.
-    if (a < 0.25f) m = 0;
-    else if (a == 0.25f) m = 0;
-    else if (a < 0.75f) m = 1;
-    else if (a == 0.75f) m = 2;
-    else if (a < 1.25f) m = 2;
-    else if (a == 1.25f) m = 2;
-    else if (a < 1.75f) m = 3;
-    else if (a == 1.75f) m = 4;
-    else if (a < 2.5f) m = 4;
-    else if (a == 2.5f) m = 4;
-    else if (a < 3.5f) m = 5;
-    else if (a == 3.5f) m = 6;
-    else if (a < 5.0f) m = 6;
-    else if (a == 5.0f) m = 6;
-    else m = 7;
+    const float a = fabsf(r);
+    const uint32_t m6 = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                        (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f);
+    const uint32_t m = a <= 5.0f ? m6 : 7u;
     return (m != 0 && r < 0.0f) ? (m | 8u) : m;
 }
 
