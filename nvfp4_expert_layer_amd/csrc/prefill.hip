@@ -70,7 +70,9 @@ constexpr int kPLds = kPOffR + kPRSlots * kPRaw;   // 150 KB
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z) with the hardware exponential and reciprocal (each
+// within ~1 ulp) in place of a correctly rounded division; z -> -inf gives -0.
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Byte offset of 16-byte chunk c of row r in a swizzled [rows][64 x 16-bit]
 // tile.  Any 8 consecutive rows (aligned) put a given chunk in 8 different
