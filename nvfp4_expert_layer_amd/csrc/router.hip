@@ -341,6 +341,9 @@ constexpr int kWideSelectTokens = 512;
 // (four slower).  Against the workgroup per token below 512: T = 129 30.6 /
 // 33.7, T = 256 33.5 / 35.9.
 constexpr int kSplitSelectTokens = 1024;
+// From kOccSelectTokens the one-wave-per-token kernel is held to 128 VGPRs, for
+// four waves per SIMD instead of three (a few registers then spill).
+constexpr int kOccSelectTokens = 4096;
 
 // Wave-wide unsigned max through DPP row shifts and row broadcasts (lanes that
 // read outside their row get 0, the identity): after the row_shr steps lane 15
@@ -565,15 +568,15 @@ constexpr int kWGroup = 8;          // candidates scored together
 // added in wave order; one wave then ranks.  A token's latency is a chain of
 // dependent round trips (the candidates' chunks above all), which the split
 // shortens where few tokens leave the chip idle.
-template <int kWSlots, int WPT>
-__global__ __launch_bounds__(64 * kWTok) void router_select_wave_kernel(
+template <int kWSlots, int WPT, int OCC = 1>
+__global__ __launch_bounds__(64 * kWTok) __attribute__((amdgpu_waves_per_eu(OCC))) void router_select_wave_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ G, const float* __restrict__ part,
     const double* __restrict__ xn2, const double* __restrict__ gn2, int T, int E, int d, int KS,
     int topk, int offset, int L, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ local_ids) {
     static_assert(WPT == 1 || WPT == kWTok, "one token per wave or per workgroup");
-    __shared__ int32_t s_cid[kWTok][kMaxExperts];
-    __shared__ double s_csc[kWTok][kMaxExperts];
+    __shared__ int32_t s_cid[kWTok][kWSlots * 64];       // candidates are experts: at most E <= 64 kWSlots
+    __shared__ double s_csc[kWTok][kWSlots * 64];
     __shared__ int32_t s_sel_id[kWTok][32];
     __shared__ double s_sel_sc[kWTok][32];
     __shared__ double s_share[WPT > 1 ? WPT : 1][kWGroup];
@@ -1310,7 +1313,8 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
         } else {
             dim3 g2((a.T + kWTok - 1) / kWTok);
             auto k = a.E <= 128 ? router_select_wave_kernel<2, 1>
-                     : a.E <= 320 ? router_select_wave_kernel<5, 1>
+                     : a.E <= 320 ? (a.T >= kOccSelectTokens ? router_select_wave_kernel<5, 1, 4>
+                                                              : router_select_wave_kernel<5, 1>)
                      : a.E <= 512 ? router_select_wave_kernel<8, 1>
                                   : router_select_wave_kernel<kMaxExperts / 64, 1>;
             hipLaunchKernelGGL(k, g2, dim3(64 * kWTok), 0, s, a.X, a.G, a.part, a.xn2, a.gn2, a.T, a.E, a.d, KS,
