@@ -96,6 +96,24 @@ def test_route_wide_select_zero_tokens_and_shard(T):
     log(f"  wide select: ambiguous {amb}, differing {diff}, P={P}")
 
 
+@pytest.mark.parametrize("T,E", [(4096, 200), (4100, 136), (4160, 320)])
+def test_route_wide_logits_ragged(T, E):
+    """From 4096 tokens and for 129..320 experts the certified logits run on
+    workgroups of 64 tokens x all experts, in K slices: expert counts that
+    leave part of the staged rows and of the last wave's columns empty, a
+    token count that leaves the last workgroup partly empty, and zero tokens,
+    against the oracle (ids bit-exact, weights, permutation)."""
+    require_gpu()
+    w = workloads.replace(workloads.WORKLOADS["decode_shard0_w4a16"], T=T, E=E, L=E // 2, offset=E // 4)
+    log(f"wide logits T={T} E={E}")
+    x = workloads.gen_hidden(w, "cuda")
+    x[T - 1] = 0
+    G = workloads.gen_gate(w, "cuda")
+    amb, diff, P = _check(x, G, w, w.offset, w.L)
+    log(f"  ambiguous {amb}, differing {diff}, P={P}")
+    assert P > 0
+
+
 def test_route_tiny_problem_odd_shapes():
     """T not a multiple of any tile, E not a multiple of 64, k = 1 and k = E."""
     require_gpu()
