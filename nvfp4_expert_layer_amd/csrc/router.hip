@@ -1273,10 +1273,14 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 int router_ksplit(int T, int E, int d) {
-    // (the wide kernel: one workgroup per 64 tokens, enough slices for ~256)
+    // Enough slices for ~512 workgroups of the 64 x 64 kernel; for the wide
+    // kernel (one workgroup per 64 tokens) ~256; for 512..1023 tokens ~192,
+    // since the four-wave select kernel loads the slices in batches of four
+    // (T = 512: 13 -> 5 slices, logits 11.2 -> 12.5 us, select 22.6 -> 18.8 us;
+    // T = 768: 12.5 -> 14.5 and 29.0 -> 24.4 us; 128 measured worse at 768).
     int base = router_wide(T, E) ? (T + kWideTok - 1) / kWideTok
                                  : ((T + kR1Tile - 1) / kR1Tile) * ((E + kR1Tile - 1) / kR1Tile);
-    const int want = router_wide(T, E) ? 256 : 512;
+    const int want = router_wide(T, E) ? 256 : (T >= kWideSelectTokens && T < kSplitSelectTokens ? 192 : 512);
     if (base < 1) return 1;                      // empty batch
     int ks = (want + base - 1) / base;
     int maxks = d / 256 > 0 ? d / 256 : 1;

@@ -38,12 +38,12 @@ def k_slices(T, E, d):
     """The number of K slices the certified logits kernel splits d into: with
     at most 320 experts (more than 128) and at least 4096 tokens, one
     workgroup per 64 tokens and enough slices for ~256 workgroups; otherwise
-    64 x 64 output tiles and enough slices for ~512; at most 16 and at most
-    d / 256 either way."""
+    64 x 64 output tiles and enough slices for ~512 (~192 from 512 to 1023
+    tokens); at most 16 and at most d / 256 either way."""
     if 128 < E <= 320 and T >= 4096:
         base, want = -(-T // 64), 256
     else:
-        base, want = -(-T // 64) * -(-E // 64), 512
+        base, want = -(-T // 64) * -(-E // 64), (192 if 512 <= T < 1024 else 512)
     ks = -(-want // base)
     return max(1, min(ks, 16, max(1, d // 256)))
 
