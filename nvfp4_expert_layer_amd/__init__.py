@@ -101,15 +101,16 @@ def _check(status):
                             lib().moe_nvfp4_strerror(status).decode())
 
 
-def _ptr(t):
+def _ptr(t, cur=None):
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensor must be on the GPU")
     # the library launches on the current device (and the stream): a tensor of
     # another device would be read through pointers that device does not map
-    cur = torch.cuda.current_device()
-    if t.device.index != cur:
+    if cur is None:
+        cur = torch.cuda.current_device()
+    if t.get_device() != cur:
         raise ValueError(f"tensor is on {t.device}, the current device is cuda:{cur}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
@@ -120,15 +121,38 @@ def _ptrs(*specs):
     """Device pointers of the tensors of specs (tensor, name, dtype, shape), after
     checking every tensor's dtype and shape (a None entry of `shape` matches any
     size) -- the library reads and writes exactly these extents, so a smaller
-    tensor would be accessed out of bounds.  None tensors pass as NULL."""
+    tensor would be accessed out of bounds.  None tensors pass as NULL.  The
+    current device is looked up once per call."""
     for t, name, dtype, shape in specs:
         if t is None:
             continue
         if t.dtype != dtype:
             raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
-        if t.dim() != len(shape) or any(s is not None and t.shape[i] != s for i, s in enumerate(shape)):
-            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
-    return [_ptr(t) for t, *_ in specs]
+        ts = t.shape
+        if ts != shape and (len(ts) != len(shape) or
+                            any(want is not None and ts[i] != want for i, want in enumerate(shape))):
+            raise ValueError(f"{name}: shape {tuple(ts)}, expected {tuple(shape)}")
+    cur = None
+    ptrs = []
+    for t, *_ in specs:
+        if cur is None and t is not None and t.is_cuda:
+            cur = torch.cuda.current_device()
+        ptrs.append(_ptr(t, cur))
+    return ptrs
+
+
+def _layer_ptrs(p, specs, local, shared):
+    """_ptrs of the token tensors `specs` and of the local and shared experts'
+    tensors; returns (token pointers, local weights struct, shared struct or None)."""
+    d, F = p.d_model, p.d_ff
+    specs = specs + local.specs(p.num_local_experts, d, F, "local")
+    if shared is not None:
+        specs += shared.specs(1, d, F, "shared")
+    ptrs = _ptrs(*specs)
+    n = len(specs) - (12 if shared is not None else 6)
+    lw = moe_nvfp4_weights(*ptrs[n:n + 6])
+    sw = moe_nvfp4_weights(*ptrs[n + 6:]) if shared is not None else None
+    return ptrs[:n], lw, sw
 
 
 def _rows(p):
@@ -138,9 +162,9 @@ def _rows(p):
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
     cur = torch.cuda.current_device()
-    if s.device.index != cur:
+    s = torch.cuda.current_stream(cur) if stream is None else stream
+    if s.device_index != cur:
         raise ValueError(f"stream is on {s.device}, the current device is cuda:{cur}")
     return ctypes.c_void_p(s.cuda_stream)
 
@@ -251,15 +275,10 @@ def alloc_workspace(problem, device="cuda"):
 
 
 def _forward_args(p, hidden, gate_w, local, shared, workspace, out):
-    T, d, F, bf = _rows(p), p.d_model, p.d_ff, torch.bfloat16
-    specs = [(hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)),
-             (workspace, "workspace", torch.uint8, (None,)), (out, "out", bf, (T, d))]
-    specs += local.specs(p.num_local_experts, d, F, "local")
-    if shared is not None:
-        specs += shared.specs(1, d, F, "shared")
-    h, g, ws, o = _ptrs(*specs)[:4]
-    lw = local.c_struct()
-    sw = shared.c_struct() if shared is not None else None
+    T, d, bf = _rows(p), p.d_model, torch.bfloat16
+    (h, g, ws, o), lw, sw = _layer_ptrs(p, [
+        (hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)),
+        (workspace, "workspace", torch.uint8, (None,)), (out, "out", bf, (T, d))], local, shared)
     return (ctypes.byref(p), h, g, ctypes.byref(lw), ctypes.byref(sw) if sw is not None else None,
             ws, workspace.numel(), o)
 
@@ -290,14 +309,10 @@ def moe_nvfp4_forward_noalloc(problem, hidden, gate_w, local, shared, out, strea
     """moe_nvfp4_forward without a workspace: the library's own per-device
     scratch (NOALLOC_SCRATCH_BYTES) serves; problems needing more raise.  Calls
     that overlap on one device race (they share the scratch)."""
-    p, T, d, F, bf = problem, _rows(problem), problem.d_model, problem.d_ff, torch.bfloat16
-    specs = [(hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)), (out, "out", bf, (T, d))]
-    specs += local.specs(p.num_local_experts, d, F, "local")
-    if shared is not None:
-        specs += shared.specs(1, d, F, "shared")
-    h, g, o = _ptrs(*specs)[:3]
-    lw = local.c_struct()
-    sw = shared.c_struct() if shared is not None else None
+    p, T, d, bf = problem, _rows(problem), problem.d_model, torch.bfloat16
+    (h, g, o), lw, sw = _layer_ptrs(p, [
+        (hidden, "hidden", bf, (T, d)), (gate_w, "gate_w", bf, (p.num_experts, d)),
+        (out, "out", bf, (T, d))], local, shared)
     _check(lib().moe_nvfp4_forward_noalloc(ctypes.byref(p), h, g, ctypes.byref(lw),
                                            ctypes.byref(sw) if sw is not None else None, o, _stream(stream)))
     return out

@@ -112,10 +112,10 @@ def test_tensors_and_stream_of_another_device_are_refused(monkeypatch):
     another device is refused before any pointer reaches it."""
     from types import SimpleNamespace
     monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
-    other = SimpleNamespace(is_cuda=True, device=torch.device("cuda", 1), is_contiguous=lambda: True,
-                            data_ptr=lambda: 0)
+    other = SimpleNamespace(is_cuda=True, device=torch.device("cuda", 1), get_device=lambda: 1,
+                            is_contiguous=lambda: True, data_ptr=lambda: 0)
     with pytest.raises(ValueError, match="current device is cuda:0"):
         nv._ptr(other)
-    stream = SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=0)
+    stream = SimpleNamespace(device=torch.device("cuda", 1), device_index=1, cuda_stream=0)
     with pytest.raises(ValueError, match="current device is cuda:0"):
         nv._stream(stream)
