@@ -119,3 +119,24 @@ def test_tensors_and_stream_of_another_device_are_refused(monkeypatch):
     stream = SimpleNamespace(device=torch.device("cuda", 1), device_index=1, cuda_stream=0)
     with pytest.raises(ValueError, match="current device is cuda:0"):
         nv._stream(stream)
+
+
+def test_weight_structs_carry_each_tensor_in_its_field(monkeypatch):
+    """The forward's weight structs are built from the checked pointers: each
+    field must hold the pointer of the tensor of the same name (local and shared)."""
+    import ctypes
+    monkeypatch.setattr(nv, "_ptr", lambda t, cur=None: None if t is None else ctypes.c_void_p(id(t)))
+    a = args()
+    fields = ("w13", "w13_scale", "w13_global", "w2", "w2_scale", "w2_global")
+    for shared in (a["shared"], None):
+        out = nv._forward_args(a["problem"], a["hidden"], a["gate_w"], a["local"], shared, a["workspace"], a["out"])
+        h, g, ws, o = out[1], out[2], out[5], out[7]
+        assert (h.value, g.value, ws.value, o.value) == (id(a["hidden"]), id(a["gate_w"]), id(a["workspace"]),
+                                                         id(a["out"]))
+        lw = out[3]._obj
+        assert [getattr(lw, f) for f in fields] == [id(getattr(a["local"], f)) for f in fields]
+        if shared is None:
+            assert out[4] is None
+        else:
+            sw = out[4]._obj
+            assert [getattr(sw, f) for f in fields] == [id(getattr(shared, f)) for f in fields]
