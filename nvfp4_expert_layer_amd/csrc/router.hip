@@ -580,7 +580,12 @@ __global__ __launch_bounds__(64 * kWTok) __attribute__((amdgpu_waves_per_eu(OCC)
     __shared__ int32_t s_sel_id[kWTok][32];
     __shared__ double s_sel_sc[kWTok][32];
     __shared__ double s_share[WPT > 1 ? WPT : 1][kWGroup];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // (held to fewer registers, the kernel keeps its wave-uniform values -- the
+    // wave index and the candidates' row addresses -- in scalar registers: at
+    // four waves per SIMD, T = 8192 83.7 -> 78.6 us, 16384 147.7 -> 139.8; with
+    // no register limit that measured 1-5% slower, so it is left to the compiler)
+    const int lane = threadIdx.x & 63;
+    const int w = OCC > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : (int)(threadIdx.x >> 6);
     const int sub = w % WPT;                             // this wave's share of the token's K chunks
     const int t = blockIdx.x * (kWTok / WPT) + w / WPT;
     // whole wave (WPT == 1: no workgroup barriers below), or whole workgroup
@@ -681,7 +686,10 @@ __global__ __launch_bounds__(64 * kWTok) __attribute__((amdgpu_waves_per_eu(OCC)
         const int ng = min(kWGroup, nc - g0);
         const uint16_t* grow[kWGroup];
 #pragma unroll
-        for (int c = 0; c < kWGroup; ++c) grow[c] = G + (size_t)cid[g0 + (c < ng ? c : 0)] * d;
+        for (int c = 0; c < kWGroup; ++c) {
+            const int id = cid[g0 + (c < ng ? c : 0)];
+            grow[c] = G + (size_t)(OCC > 1 ? __builtin_amdgcn_readfirstlane(id) : id) * d;
+        }
         double acc[kWGroup];
 #pragma unroll
         for (int c = 0; c < kWGroup; ++c) acc[c] = 0.0;
